@@ -1,0 +1,198 @@
+"""CPU oracle for the sparse top-k MoE FFN forward — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product path (the HIP library and its
+binding) never imports, links or calls it, and the two share no code.
+
+``liboracle.so`` (plain C, fp64, OpenMP) implements the per-token loop of the
+"moe-training" SKILL page's reference layer (Quick Start, Basic MoE
+Architecture), the losses of Core Concepts 3 (Load Balancing) and capacity
+dropping in token order.  This module is argument marshalling around it, plus
+``forward()``, which strings the steps together in the page's order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+# MOE_ORACLE_LIB may point at another build of moe_oracle.c (used by the test
+# that plants mistakes in the oracle source to show the pins catch them).
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("cf", ctypes.c_double),
+                ("dtype", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER(_Problem)
+        vp = ctypes.c_void_p
+        L.orc_logits.argtypes = [P, vp, vp, vp, vp]
+        L.orc_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_capacity.argtypes = [P]
+        L.orc_capacity.restype = ctypes.c_int64
+        L.orc_dispatch.argtypes = [P, vp, vp, vp, vp]
+        L.orc_expert_rows.argtypes = [P, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
+        L.orc_forward_tokens.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_int64, vp]
+        L.orc_combine.argtypes = [P, vp, vp, vp, vp]
+        L.orc_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def problem(spec, **over) -> _Problem:
+    """Build the oracle's problem struct from an inputs.Spec (fields T, H, E, k,
+    F, cf, dtype), with optional overrides."""
+    g = lambda n: over.get(n, getattr(spec, n))
+    return _Problem(T=int(g("T")), H=int(g("H")), E=int(g("E")), k=int(g("k")),
+                    F=int(g("F")), cf=float(g("cf")),
+                    dtype=1 if g("dtype") == "bf16" else 0, pad_=0)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _storage(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    want = np.uint16 if dtype == "bf16" else np.float32
+    if a.dtype != want:
+        raise TypeError(f"oracle expects {want} storage for {dtype}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def capacity(spec) -> int:
+    return int(lib().orc_capacity(ctypes.byref(problem(spec))))
+
+
+def logits(spec, x, Wg, bg=None) -> np.ndarray:
+    d = spec.dtype
+    x, Wg, bg = _storage(x, d), _storage(Wg, d), _storage(bg, d)
+    out = np.empty((spec.T, spec.E), np.float64)
+    _check(lib().orc_logits(ctypes.byref(problem(spec)), _ptr(x), _ptr(Wg), _ptr(bg),
+                            _ptr(out)), "logits")
+    return out
+
+
+def route(spec, lg: np.ndarray) -> Dict[str, np.ndarray]:
+    lg = np.ascontiguousarray(lg, np.float64)
+    T, E, k = spec.T, spec.E, spec.k
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    probs = np.empty((T, E), np.float64)
+    lse = np.empty((T,), np.float64)
+    counts = np.empty((E,), np.int32)
+    aux = ctypes.c_double()
+    z = ctypes.c_double()
+    _check(lib().orc_route(ctypes.byref(problem(spec)), _ptr(lg), _ptr(idx), _ptr(w),
+                           _ptr(probs), _ptr(lse), _ptr(counts), ctypes.byref(aux),
+                           ctypes.byref(z)), "route")
+    return dict(topk_idx=idx, topk_w=w, probs=probs, lse=lse, counts=counts,
+                aux=aux.value, z=z.value)
+
+
+def dispatch(spec, topk_idx: np.ndarray) -> Dict[str, np.ndarray]:
+    T, E, k = spec.T, spec.E, spec.k
+    idx = np.ascontiguousarray(topk_idx, np.int32)
+    offsets = np.empty((E + 1,), np.int32)
+    pos = np.empty((T, k), np.int32)
+    row_token = np.empty((T * k,), np.int32)
+    _check(lib().orc_dispatch(ctypes.byref(problem(spec)), _ptr(idx), _ptr(offsets),
+                              _ptr(pos), _ptr(row_token)), "dispatch")
+    return dict(offsets=offsets, pos=pos, row_token=row_token)
+
+
+def expert_rows(spec, rows, experts, W1, b1, W2, b2, want_h: bool = True):
+    d = spec.dtype
+    rows = _storage(rows, d)
+    n = rows.shape[0]
+    ex = np.ascontiguousarray(experts, np.int32)
+    h = np.empty((n, spec.F), np.float64) if want_h else None
+    y = np.empty((n, spec.H), np.float64)
+    _check(lib().orc_expert_rows(ctypes.byref(problem(spec)), _ptr(rows), n, _ptr(ex),
+                                 _ptr(_storage(W1, d)), _ptr(_storage(b1, d)),
+                                 _ptr(_storage(W2, d)), _ptr(_storage(b2, d)),
+                                 _ptr(h), _ptr(y)), "expert_rows")
+    return h, y
+
+
+def forward_tokens(spec, x, topk_idx, topk_w, pos, W1, b1, W2, b2,
+                   tokens: Sequence[int]) -> np.ndarray:
+    d = spec.dtype
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    out = np.empty((tok.shape[0], spec.H), np.float64)
+    _check(lib().orc_forward_tokens(
+        ctypes.byref(problem(spec)), _ptr(_storage(x, d)),
+        _ptr(np.ascontiguousarray(topk_idx, np.int32)),
+        _ptr(np.ascontiguousarray(topk_w, np.float64)),
+        _ptr(np.ascontiguousarray(pos, np.int32)), _ptr(_storage(W1, d)),
+        _ptr(_storage(b1, d)), _ptr(_storage(W2, d)), _ptr(_storage(b2, d)),
+        _ptr(tok), tok.shape[0], _ptr(out)), "forward_tokens")
+    return out
+
+
+def combine(spec, y, pos, topk_w) -> np.ndarray:
+    out = np.empty((spec.T, spec.H), np.float64)
+    _check(lib().orc_combine(ctypes.byref(problem(spec)), _ptr(_storage(y, spec.dtype)),
+                             _ptr(np.ascontiguousarray(pos, np.int32)),
+                             _ptr(np.ascontiguousarray(topk_w, np.float64)), _ptr(out)),
+           "combine")
+    return out
+
+
+def forward(spec, inp: Dict[str, Optional[np.ndarray]], tokens: Optional[Sequence[int]] = None,
+            given_logits: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """The whole layer: logits -> routing and losses -> capacity dispatch ->
+    expert FFN and combine.  `tokens` restricts the (expensive) FFN/combine to
+    a subset of token rows (out then has one row per listed token); routing
+    and dispatch always cover all T tokens because capacity dropping depends
+    on every earlier token.  `given_logits` replaces the gate linear (e.g. by
+    logits the GPU produced, so both sides take top-k decisions on the same
+    values)."""
+    lg = logits(spec, inp["x"], inp["Wg"], inp.get("bg")) if given_logits is None \
+        else np.ascontiguousarray(given_logits, np.float64)
+    r = route(spec, lg)
+    dsp = dispatch(spec, r["topk_idx"])
+    toks = np.arange(spec.T) if tokens is None else np.asarray(tokens, np.int64)
+    out = forward_tokens(spec, inp["x"], r["topk_idx"], r["topk_w"], dsp["pos"],
+                         inp["W1"], inp.get("b1"), inp["W2"], inp.get("b2"), toks)
+    res: Dict[str, object] = dict(logits=lg, cap=capacity(spec), out=out, tokens=toks)
+    res.update(r)
+    res.update(dsp)
+    return res
+
+
+def topk_margin(spec, lg: np.ndarray) -> float:
+    """Smallest gap between the k-th and (k+1)-th largest logit of any token
+    (infinite when k == E).  Used to decide whether top-k decisions taken on
+    differently rounded logits are guaranteed to agree."""
+    if spec.k >= spec.E:
+        return float("inf")
+    s = -np.sort(-np.asarray(lg, np.float64), axis=1)
+    return float(np.min(s[:, spec.k - 1] - s[:, spec.k]))

@@ -1,0 +1,174 @@
+"""Independent formulations of the MoE layer used to pin the C oracle —
+TEST INFRASTRUCTURE ONLY (imported by tests, never by the product path).
+
+Each function computes the same layer as ``liboracle.so`` by a different
+route, from library primitives, so that a slip in the per-token C loop (a
+dropped term, a wrong sign or index, a transposed operand) shows up as a
+mismatch:
+
+* ``dense_then_mask`` — evaluate EVERY expert on EVERY token with dense
+  matrix products, then gather the selected outputs by index and weight them.
+  This is the "evaluate all experts, then index by the top-k" reading of the
+  "moe-training" SKILL page's Top-2 routing snippet (Core Concepts,
+  2. Routing Mechanisms).  Top-k here is a stable descending sort of the
+  softmax probabilities; capacity ranks come from a cumulative sum of one-hot
+  rows in token order.
+* ``torch_masked_layer`` — the reference layer of the page (Quick Start, Basic
+  MoE Architecture) built from ``torch.nn.Linear`` / ``torch.nn.GELU`` /
+  ``torch.softmax`` / ``torch.topk`` in float64 on the CPU, dispatching with
+  one boolean row mask per expert (no capacity limit).
+* ``torch_expert_major`` — the expert-major formulation of the page's Mixtral
+  block (Advanced Patterns, Mixtral 8x7B Architecture): per-expert gather of
+  the (token, slot) pairs and ``index_add_`` back into token rows, with the
+  GELU experts and biases of the reference layer (no capacity limit).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+from scipy import special
+
+from workloads import to_f32
+
+
+def _f64(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    return None if a is None else to_f32(a, dtype).astype(np.float64)
+
+
+def _capacity(spec) -> int:
+    if not spec.cf > 0:
+        return spec.T
+    return int(np.ceil(spec.cf * spec.T * spec.k / spec.E))
+
+
+def dense_then_mask(spec, inp: Dict[str, Optional[np.ndarray]]) -> Dict[str, object]:
+    d = spec.dtype
+    T, H, E, k, F = spec.T, spec.H, spec.E, spec.k, spec.F
+    x = _f64(inp["x"], d)
+    Wg = _f64(inp["Wg"], d)
+    bg = _f64(inp.get("bg"), d)
+    W1 = _f64(inp["W1"], d)
+    W2 = _f64(inp["W2"], d)
+    b1 = _f64(inp.get("b1"), d)
+    b2 = _f64(inp.get("b2"), d)
+
+    lg = x @ Wg + (0.0 if bg is None else bg[None, :])
+    p = special.softmax(lg, axis=1)
+    lse = special.logsumexp(lg, axis=1)
+    idx = np.argsort(-p, axis=1, kind="stable")[:, :k].astype(np.int32)
+    psel = np.take_along_axis(p, idx, axis=1)
+    w = psel / psel.sum(axis=1, keepdims=True)
+
+    f = np.bincount(idx.ravel(), minlength=E) / float(T * k)
+    aux = E * float(np.sum(f * p.mean(axis=0)))
+    z = float(np.mean(lse ** 2))
+
+    cap = _capacity(spec)
+    onehot = np.zeros((T * k, E), np.int64)
+    onehot[np.arange(T * k), idx.ravel()] = 1
+    rank = (np.cumsum(onehot, axis=0) - 1)[np.arange(T * k), idx.ravel()]
+    kept = rank < cap
+    kept_per_e = np.bincount(idx.ravel()[kept], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(kept_per_e)]).astype(np.int32)
+    pos = np.where(kept, offsets[idx.ravel()] + rank, -1).reshape(T, k).astype(np.int32)
+
+    # every expert on every token
+    Y = np.empty((E, T, H))
+    for e in range(E):
+        a = x @ W1[e] + (0.0 if b1 is None else b1[e][None, :])
+        g = 0.5 * a * (1.0 + special.erf(a / np.sqrt(2.0)))
+        Y[e] = g @ W2[e] + (0.0 if b2 is None else b2[e][None, :])
+    sel = Y[idx, np.arange(T)[:, None], :]           # [T, k, H]
+    coef = w * kept.reshape(T, k)
+    out = np.einsum("tk,tkh->th", coef, sel)
+    return dict(logits=lg, probs=p, lse=lse, topk_idx=idx, topk_w=w, counts=np.bincount(
+        idx.ravel(), minlength=E).astype(np.int32), aux=aux, z=z, cap=cap, offsets=offsets,
+        pos=pos, out=out, Y=Y)
+
+
+def _torch_modules(spec, inp):
+    import torch
+    d = spec.dtype
+    E = spec.E
+    t64 = lambda a: None if a is None else torch.from_numpy(_f64(a, d))
+    W1, W2, b1, b2 = t64(inp["W1"]), t64(inp["W2"]), t64(inp.get("b1")), t64(inp.get("b2"))
+    Wg, bg = t64(inp["Wg"]), t64(inp.get("bg"))
+    experts = []
+    for e in range(E):
+        l1 = torch.nn.Linear(spec.H, spec.F, bias=b1 is not None, dtype=torch.float64)
+        l2 = torch.nn.Linear(spec.F, spec.H, bias=b2 is not None, dtype=torch.float64)
+        with torch.no_grad():
+            l1.weight.copy_(W1[e].T)          # nn.Linear stores [out, in]
+            l2.weight.copy_(W2[e].T)
+            if b1 is not None:
+                l1.bias.copy_(b1[e])
+            if b2 is not None:
+                l2.bias.copy_(b2[e])
+        experts.append(torch.nn.Sequential(l1, torch.nn.GELU(), l2))
+    gate = torch.nn.Linear(spec.H, E, bias=bg is not None, dtype=torch.float64)
+    with torch.no_grad():
+        gate.weight.copy_(Wg.T)
+        if bg is not None:
+            gate.bias.copy_(bg)
+    return gate, experts
+
+
+def torch_masked_layer(spec, inp) -> Dict[str, object]:
+    """Token-choice routing with library top-k, then one boolean row mask per
+    expert: rows that picked expert e get that expert's output scaled by the
+    weight they gave it (an expert appears at most once in a token's top-k, so
+    the slots of a token can be merged).  No capacity limit."""
+    import torch
+    gate, experts = _torch_modules(spec, inp)
+    xt = torch.from_numpy(_f64(inp["x"], spec.dtype))
+    with torch.no_grad():
+        lg = gate(xt)
+        prob = torch.softmax(lg, dim=-1)
+        val, sel = torch.topk(prob, spec.k, dim=-1)
+        wts = val / val.sum(dim=-1, keepdim=True)
+        acc = torch.zeros_like(xt)
+        for e, net in enumerate(experts):
+            hit = sel == e
+            rows = hit.any(dim=1)
+            if not bool(rows.any()):
+                continue
+            coef = (wts * hit).sum(dim=1)[rows]
+            acc[rows] += coef[:, None] * net(xt[rows])
+        hist = torch.nn.functional.one_hot(sel.reshape(-1).long(), spec.E).sum(dim=0)
+        aux = spec.E * torch.dot(hist.double() / sel.numel(), prob.mean(dim=0))
+        z = torch.logsumexp(lg, dim=-1).square().mean()
+    return dict(logits=lg.numpy(), topk_idx=sel.numpy().astype(np.int32),
+                topk_w=wts.numpy(), out=acc.numpy(), aux=float(aux), z=float(z))
+
+
+def torch_expert_major(spec, inp) -> np.ndarray:
+    """Expert-major accumulation: for each expert, the flat (token, slot) pairs
+    that chose it are gathered, run through the expert, scaled by their weight
+    and added into their token rows with index_add_.  No capacity limit."""
+    import torch
+    gate, experts = _torch_modules(spec, inp)
+    xt = torch.from_numpy(_f64(inp["x"], spec.dtype))
+    with torch.no_grad():
+        prob = torch.softmax(gate(xt), dim=1)
+        val, sel = torch.topk(prob, spec.k, dim=-1)
+        wflat = (val / val.sum(dim=-1, keepdim=True)).reshape(-1)
+        eflat = sel.reshape(-1)
+        tflat = torch.arange(spec.T).repeat_interleave(spec.k)
+        acc = torch.zeros_like(xt)
+        for e, net in enumerate(experts):
+            j = torch.nonzero(eflat == e).squeeze(1)
+            if j.numel() == 0:
+                continue
+            toks = tflat[j]
+            acc.index_add_(0, toks, net(xt[toks]) * wflat[j, None])
+    return acc.numpy()
+
+
+def dense_ffn(spec, inp, e: int = 0) -> np.ndarray:
+    """One expert applied densely to every token with torch.nn modules (float64)."""
+    import torch
+    _, experts = _torch_modules(spec, inp)
+    x = torch.from_numpy(_f64(inp["x"], spec.dtype))
+    with torch.no_grad():
+        return experts[e](x).numpy()

@@ -1,0 +1,84 @@
+/*
+ * CPU oracle for the sparse top-k MoE FFN forward — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests, the package smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  The product path never calls it.
+ *
+ * It is a plain, slow, per-token fp64 implementation of the layer described
+ * by the "moe-training" SKILL page (Quick Start, Basic MoE Architecture:
+ * gate Linear -> softmax -> top-k -> renormalise -> per-expert
+ * Linear(H,4H) -> GELU -> Linear(4H,H) -> weighted sum) together with the
+ * load-balancing and router z-losses (Core Concepts, 3. Load Balancing) and
+ * capacity-factor dropping (Core Concepts, 4. Expert Parallelism; Best
+ * Practices, 2. Capacity Factor Tuning).
+ *
+ * Storage: inputs are read as fp32 values (dtype 0) or bf16 bit patterns
+ * (dtype 1, uint16) and widened exactly to double; every sum is in double with
+ * no intermediate rounding.  Weight layout is [in][out]: Wg[H][E],
+ * W1[E][H][F], W2[E][F][H].  Null bias pointers mean zero bias.
+ *
+ * All functions return 0 on success and a negative value on a bad argument.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int64_t T;      /* tokens */
+    int32_t H;      /* hidden width */
+    int32_t E;      /* experts */
+    int32_t k;      /* experts per token */
+    int32_t F;      /* expert inner width (4H on the pages) */
+    double  cf;     /* capacity factor; <= 0 means no capacity limit */
+    int32_t dtype;  /* 0: fp32 storage, 1: bf16 storage */
+    int32_t pad_;
+} orc_problem;
+
+/* Gate logits l[t][e] = bg[e] + sum_i x[t][i] * Wg[i][e]  (double, [T][E]). */
+int orc_logits(const orc_problem* p, const void* x, const void* Wg, const void* bg,
+               double* logits);
+
+/* Softmax, top-k (descending; equal values: lower expert index first),
+ * renormalised weights, pre-capacity counts, aux and z losses, from logits.
+ * probs [T][E] and lse [T] are optional (may be NULL). */
+int orc_route(const orc_problem* p, const double* logits, int32_t* topk_idx,
+              double* topk_w, double* probs, double* lse, int32_t* counts,
+              double* aux, double* z);
+
+/* Expert capacity: T when cf <= 0, else ceil(cf * T * k / E). */
+int64_t orc_capacity(const orc_problem* p);
+
+/* Token-order dispatch with capacity dropping: offsets [E+1], pos [T][k]
+ * (-1 = dropped), row_token [T*k] (entries >= offsets[E] set to -1). */
+int orc_dispatch(const orc_problem* p, const int32_t* topk_idx, int32_t* offsets,
+                 int32_t* pos, int32_t* row_token);
+
+/* Expert FFN on n rows: rows[r] (storage type, [n][H]) through expert
+ * experts[r]; writes GELU outputs h [n][F] (optional) and y [n][H]. */
+int orc_expert_rows(const orc_problem* p, const void* rows, int64_t n,
+                    const int32_t* experts, const void* W1, const void* b1,
+                    const void* W2, const void* b2, double* h, double* y);
+
+/* Layer output for the listed tokens: out[j][o] for token tokens[j], given the
+ * routing (topk_idx, topk_w) and dispatch (pos).  out is [ntok][H]. */
+int orc_forward_tokens(const orc_problem* p, const void* x, const int32_t* topk_idx,
+                       const double* topk_w, const int32_t* pos, const void* W1,
+                       const void* b1, const void* W2, const void* b2,
+                       const int64_t* tokens, int64_t ntok, double* out);
+
+/* Weighted combine of given expert-output rows y [A][H] (storage type):
+ * out[t] = sum over kept slots s, in slot order, of w[t][s] * y[pos[t][s]]. */
+int orc_combine(const orc_problem* p, const void* y, const int32_t* pos,
+                const double* topk_w, double* out);
+
+/* Number of OpenMP threads the oracle uses. */
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

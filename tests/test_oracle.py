@@ -1,0 +1,278 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+The oracle (oracle/liboracle.so, a per-token fp64 C loop) is checked against
+things other than itself: the worked weights the routing diagram prints,
+closed forms (all-zero gate, constant and one-hot biases, identical experts,
+one expert, k = E), a dense evaluate-every-expert-then-mask brute force, two
+torch float64 formulations of the page's layer, and dispatch invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RT, AT = 1e-10, 1e-12
+
+
+def tiny(T=24, H=16, E=4, k=2, F=40, dtype="f32", cf=0.0, seed=7, biases=True, **kw):
+    s = W.Spec(f"tiny_T{T}_H{H}_E{E}_k{k}_F{F}_{dtype}_cf{cf}", T=T, H=H, E=E, k=k, F=F,
+               dtype=dtype, cf=cf, seed=seed, x=W.Dist("normal", 1.0),
+               wg=W.Dist("normal", 0.5), w1=W.Dist("uniform", 1 / math.sqrt(H)),
+               w2=W.Dist("uniform", 1 / math.sqrt(F)))
+    if biases:
+        s = s.replace(bg=W.Dist("uniform", 0.3), b1=W.Dist("uniform", 0.2),
+                      b2=W.Dist("uniform", 0.1))
+    return s.replace(**kw) if kw else s
+
+
+def run_oracle(om, spec, inp, **kw):
+    return om.forward(spec, inp, **kw)
+
+
+# ---------------------------------------------------------------- worked example
+def test_golden_diagram_weights(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "top2_diagram_weights.json")))
+    spec = tiny(T=1, E=g["E"], k=g["k"])
+    r = oracle_mod.route(spec, np.array([g["logits"]], np.float64))
+    assert r["topk_idx"][0].tolist() == g["expected_topk_idx"]
+    np.testing.assert_allclose(r["topk_w"][0], g["expected_topk_w"], rtol=0, atol=1e-15)
+    assert abs(r["topk_w"][0].sum() - 1.0) < 1e-15
+
+
+# ---------------------------------------------------------------- brute force
+BRUTE_CASES = [
+    dict(),
+    dict(dtype="bf16"),
+    dict(k=1),
+    dict(k=3, E=5),
+    dict(k=4, E=4),
+    dict(E=8, k=2, T=64, H=32, F=48),
+    dict(cf=0.5),
+    dict(cf=1.0, k=1, E=3, T=31),
+    dict(cf=1.25, dtype="bf16", T=50, E=6, k=2),
+    dict(biases=False),
+    dict(E=1, k=1),
+    dict(T=1),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE_CASES, ids=[str(c) for c in BRUTE_CASES])
+def test_oracle_matches_dense_brute_force(oracle_mod, case):
+    spec = tiny(**case)
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    b = bf.dense_then_mask(spec, inp)
+    np.testing.assert_allclose(o["logits"], b["logits"], rtol=RT, atol=AT)
+    assert np.array_equal(o["topk_idx"], b["topk_idx"])
+    np.testing.assert_allclose(o["topk_w"], b["topk_w"], rtol=RT, atol=AT)
+    np.testing.assert_allclose(o["probs"], b["probs"], rtol=RT, atol=AT)
+    np.testing.assert_allclose(o["lse"], b["lse"], rtol=RT, atol=AT)
+    assert np.array_equal(o["counts"], b["counts"])
+    assert o["cap"] == b["cap"]
+    assert math.isclose(o["aux"], b["aux"], rel_tol=RT)
+    assert math.isclose(o["z"], b["z"], rel_tol=RT, abs_tol=AT)
+    assert np.array_equal(o["offsets"], b["offsets"])
+    assert np.array_equal(o["pos"], b["pos"])
+    np.testing.assert_allclose(o["out"], b["out"], rtol=RT, atol=1e-11)
+
+
+def test_oracle_expert_rows_match_dense_experts(oracle_mod):
+    spec = tiny(E=3, T=20)
+    inp = W.generate(spec, workers=1)
+    b = bf.dense_then_mask(spec, inp)
+    for e in range(spec.E):
+        _, y = oracle_mod.expert_rows(spec, inp["x"], np.full(spec.T, e), inp["W1"],
+                                      inp["b1"], inp["W2"], inp["b2"])
+        np.testing.assert_allclose(y, b["Y"][e], rtol=RT, atol=1e-11)
+
+
+def test_oracle_combine_matches_indexing(oracle_mod):
+    spec = tiny(T=30, E=4, k=2, cf=0.75, dtype="bf16")
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    A = int(o["offsets"][-1])
+    y = W.synthetic_rows(spec, A)
+    out = oracle_mod.combine(spec, y, o["pos"], o["topk_w"])
+    yf = W.to_f32(y, "bf16").astype(np.float64)
+    ref = np.zeros((spec.T, spec.H))
+    for t in range(spec.T):
+        for s in range(spec.k):
+            if o["pos"][t, s] >= 0:
+                ref[t] += o["topk_w"][t, s] * yf[o["pos"][t, s]]
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- torch formulations
+def test_oracle_matches_torch_layers_on_tiny_fp32_config(oracle_mod):
+    spec = W.CONFIGS["c1"]
+    inp = W.generate(spec)
+    o = run_oracle(oracle_mod, spec, inp)
+    assert oracle_mod.topk_margin(spec, o["logits"]) > 1e-9      # no ties: torch.topk is safe
+    t = bf.torch_masked_layer(spec, inp)
+    np.testing.assert_allclose(o["logits"], t["logits"], rtol=RT, atol=AT)
+    assert np.array_equal(o["topk_idx"], t["topk_idx"])
+    np.testing.assert_allclose(o["topk_w"], t["topk_w"], rtol=RT, atol=AT)
+    np.testing.assert_allclose(o["out"], t["out"], rtol=RT, atol=1e-11)
+    assert math.isclose(o["aux"], t["aux"], rel_tol=1e-12)
+    assert math.isclose(o["z"], t["z"], rel_tol=1e-12)
+    em = bf.torch_expert_major(spec, inp)
+    np.testing.assert_allclose(o["out"], em, rtol=RT, atol=1e-11)
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("E,k", [(8, 2), (8, 1), (5, 3), (4, 4)])
+def test_zero_gate_ties_and_losses(oracle_mod, E, k):
+    spec = W.zero_gate(tiny(T=40, E=E, k=k))
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    assert np.all(o["logits"] == 0.0)
+    assert np.array_equal(o["topk_idx"], np.tile(np.arange(k, dtype=np.int32), (spec.T, 1)))
+    np.testing.assert_allclose(o["topk_w"], 1.0 / k, rtol=0, atol=1e-15)
+    expect_counts = np.zeros(E, np.int32)
+    expect_counts[:k] = spec.T
+    assert np.array_equal(o["counts"], expect_counts)
+    assert math.isclose(o["aux"], 1.0, rel_tol=1e-14)
+    assert math.isclose(o["z"], math.log(E) ** 2, rel_tol=1e-14, abs_tol=1e-15)
+
+
+def test_zero_gate_capacity_closed_form(oracle_mod):
+    spec = W.zero_gate(tiny(T=64, E=8, k=2, cf=0.5))
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    cap = o["cap"]
+    assert cap == 8                                    # ceil(0.5 * 64 * 2 / 8)
+    assert o["offsets"].tolist() == [0, 8, 16] + [16] * 6
+    for t in range(spec.T):
+        for s in range(2):
+            assert o["pos"][t, s] == (s * cap + t if t < cap else -1)
+    ffn = [bf.dense_ffn(spec, inp, e) for e in (0, 1)]
+    for t in range(spec.T):
+        ref = 0.5 * ffn[0][t] + 0.5 * ffn[1][t] if t < cap else np.zeros(spec.H)
+        np.testing.assert_allclose(o["out"][t], ref, rtol=RT, atol=1e-11)
+
+
+def test_constant_bias_z_loss(oracle_mod):
+    c, E = 1.5, 6
+    spec = W.zero_gate(tiny(T=16, E=E, k=2)).replace(bg=W.Dist("const", c))
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    assert math.isclose(o["z"], (c + math.log(E)) ** 2, rel_tol=1e-14)
+    assert math.isclose(o["aux"], 1.0, rel_tol=1e-14)
+
+
+def test_one_hot_bias_losses(oracle_mod):
+    c, E = 2.0, 8
+    spec = W.zero_gate(tiny(T=10, E=E, k=1))
+    inp = W.generate(spec, workers=1)
+    bg = np.zeros(E, np.float32)
+    bg[0] = c
+    inp["bg"] = bg
+    o = run_oracle(oracle_mod, spec, inp)
+    assert np.all(o["topk_idx"] == 0) and np.all(o["topk_w"] == 1.0)
+    p0 = math.exp(c) / (math.exp(c) + E - 1)
+    assert math.isclose(o["aux"], E * p0, rel_tol=1e-14)
+    assert math.isclose(o["z"], math.log(math.exp(c) + E - 1) ** 2, rel_tol=1e-14)
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.5])
+def test_identical_experts_reduce_to_dense_ffn(oracle_mod, cf):
+    spec = tiny(T=48, E=4, k=2, cf=cf, identical_experts=True)
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    dense = bf.dense_ffn(spec, inp, 0)
+    kept_w = np.where(o["pos"] >= 0, o["topk_w"], 0.0).sum(axis=1)
+    np.testing.assert_allclose(o["out"], kept_w[:, None] * dense, rtol=RT, atol=1e-11)
+    if cf == 0.0:
+        np.testing.assert_allclose(o["out"], dense, rtol=RT, atol=1e-11)
+    else:
+        assert (o["pos"] < 0).any()
+
+
+def test_single_expert_is_dense_ffn(oracle_mod):
+    spec = tiny(T=33, E=1, k=1)
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    assert np.all(o["topk_w"] == 1.0)
+    np.testing.assert_allclose(o["out"], bf.dense_ffn(spec, inp, 0), rtol=RT, atol=1e-11)
+    assert math.isclose(o["aux"], 1.0, rel_tol=1e-14)
+    np.testing.assert_allclose(o["lse"], o["logits"][:, 0], rtol=0, atol=1e-14)
+
+
+def test_k_equals_E_is_soft_mixture(oracle_mod):
+    spec = tiny(T=20, E=4, k=4)
+    inp = W.generate(spec, workers=1)
+    o = run_oracle(oracle_mod, spec, inp)
+    mix = sum(o["probs"][:, e:e + 1] * bf.dense_ffn(spec, inp, e) for e in range(4))
+    np.testing.assert_allclose(o["out"], mix, rtol=RT, atol=1e-11)
+    assert math.isclose(o["aux"], 1.0, rel_tol=1e-13)
+
+
+def test_top_k_tie_rule(oracle_mod):
+    spec = tiny(T=3, E=4, k=2)
+    lg = np.array([[1.0, 2.0, 2.0, 0.0], [5.0, 5.0, 5.0, 5.0], [0.0, -1.0, 3.0, 3.0]])
+    r = oracle_mod.route(spec, lg)
+    assert r["topk_idx"].tolist() == [[1, 2], [0, 1], [2, 3]]
+    np.testing.assert_allclose(r["topk_w"], 0.5, atol=1e-15)
+
+
+@pytest.mark.parametrize("T,k,E,cf,cap", [
+    (8192, 2, 8, 1.25, 2560), (8192, 1, 128, 1.25, 80), (16384, 2, 8, 2.0, 8192),
+    (16384, 2, 64, 0.0, 16384), (256, 2, 8, 0.5, 32), (10, 1, 3, 1.0, 4), (8192, 2, 8, 1.0, 2048)])
+def test_capacity_values(oracle_mod, T, k, E, cf, cap):
+    spec = tiny(T=T, k=k, E=E, cf=cf)
+    assert oracle_mod.capacity(spec) == cap
+
+
+# ---------------------------------------------------------------- invariants
+def check_dispatch_invariants(spec, o):
+    T, E, k = spec.T, spec.E, spec.k
+    idx, pos, off, rt = o["topk_idx"], o["pos"], o["offsets"], o["row_token"]
+    cap = o["cap"]
+    np.testing.assert_allclose(o["topk_w"].sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert o["counts"].sum() == T * k
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == k
+    kept = np.diff(off)
+    assert np.all(kept >= 0) and np.all(kept <= cap)
+    assert np.all(kept == np.minimum(o["counts"], cap))
+    A = int(off[-1])
+    kp = pos[pos >= 0]
+    assert kp.size == A and np.array_equal(np.sort(kp), np.arange(A))
+    for t in range(T):
+        for s in range(k):
+            r = pos[t, s]
+            if r >= 0:
+                assert rt[r] == t
+                assert off[idx[t, s]] <= r < off[idx[t, s] + 1]
+    for e in range(E):
+        seg = rt[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    assert np.all(rt[A:] == -1)
+
+
+def test_dispatch_invariants_tiny(oracle_mod):
+    spec = W.CONFIGS["c1"].replace(cf=0.5)
+    inp = W.generate(spec)
+    o = run_oracle(oracle_mod, spec, inp)
+    assert o["cap"] == 32 and (o["pos"] < 0).any()
+    check_dispatch_invariants(spec, o)
+
+
+@pytest.mark.slow
+def test_dispatch_invariants_ds_shaped_routing(oracle_mod):
+    """Routing and dispatch of the T=8192, H=1024, E=8 layer at capacity
+    factor 1.0 (forcing drops); the FFN is not evaluated here."""
+    spec = W.CONFIGS["c2"].replace(cf=1.0)
+    inp = W.generate(spec, with_weights=False)
+    lg = oracle_mod.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    o = oracle_mod.route(spec, lg)
+    o.update(oracle_mod.dispatch(spec, o["topk_idx"]))
+    o["cap"] = oracle_mod.capacity(spec)
+    assert o["cap"] == 2048
+    check_dispatch_invariants(spec, o)

@@ -1,0 +1,57 @@
+"""The oracle's pins must be able to fail: plant one plausible mistake at a time
+in a copy of oracle/moe_oracle.c (on the CPU), build it, and require that the
+pin suite (tests/test_oracle.py) rejects every planted copy."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+# name -> (text in the oracle source, planted replacement)
+MUTANTS = {
+    "drop_expert_bias2": ("y[o] += load(b2, (int64_t)e * H + o, dt);", "y[o] += 0.0;"),
+    "gelu_wrong_sign": ("(1.0 + erf(a[j] * M_SQRT1_2))", "(1.0 - erf(a[j] * M_SQRT1_2))"),
+    "aux_without_E": ("*aux = (double)E * acc;", "*aux = acc;"),
+    "tie_to_higher_index": ("if (best < 0 || l[e] > l[best]) best = e;",
+                            "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "capacity_off_by_one": ("if (fill[e] < cap) {", "if (fill[e] <= cap) {"),
+    "dropped_slot_still_added": ("if (pos[t * k + s] < 0) continue;", ""),
+    "z_not_squared": ("acc += L[t] * L[t];", "acc += L[t];"),
+    "w1_transposed": ("axpy_row(a, xr[i], W1, ((int64_t)e * H + i) * F, F, dt);",
+                      "for (int j = 0; j < F; ++j) a[j] += xr[i] * "
+                      "load(W1, (int64_t)e * H * F + (int64_t)j * H + i, dt);"),
+    "no_renormalisation": ("topk_w[t * k + s] = pt[idx[s]] / S;", "topk_w[t * k + s] = pt[idx[s]];"),
+    "lse_without_shift": ("L[t] = m + log(Z);", "L[t] = log(Z);"),
+    "gate_bias_dropped": ("for (int e = 0; e < E; ++e) l[e] += load(bg, e, dt);", ";"),
+    "offsets_shifted": ("offsets[e + 1] = offsets[e] + (int32_t)fill[e];",
+                        "offsets[e + 1] = offsets[e] + (int32_t)fill[e] + (e == 0);"),
+    "aux_counts_after_capacity": (
+        "acc += ((double)c / (double)(T * k))",
+        "acc += ((double)(c < orc_capacity(p) ? c : orc_capacity(p)) / (double)(T * k))"),
+    "slot_weights_swapped": ("const double w = topk_w[t * k + s];",
+                             "const double w = topk_w[t * k + (k - 1 - s)];"),
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(tmp_path, name):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    d = tmp_path / name
+    d.mkdir()
+    (d / "moe_oracle.c").write_text(src.replace(old, new))
+    shutil.copy(os.path.join(ROOT, "oracle", "moe_oracle.h"), d / "moe_oracle.h")
+    lib = d / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
+                    str(d / "moe_oracle.c"), "-lm"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "-m", "not slow", os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"planted mistake {name} survived the pins:\n{r.stdout[-2000:]}"
