@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: sparse top-k MoE FFN layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c5] [--no-cpu-baseline]
+
+A step is one moe_forward (router + losses, dispatch, expert FFN up and down,
+combine) over one batch of seeded synthetic input that is already resident in
+HBM.  The default workload is the Mixtral-8x7B-shaped layer (T=16384 tokens,
+H=4096, 8 experts, top-2, FFN 14336, capacity factor 2.0, bf16 storage, fp32
+accumulation).  Prints ONE JSON line.
+
+value         tokens/s = T * K / (timed wall time of K back-to-back steps)
+roofline      the dominant kernel (the larger FFN GEMM) against the dense bf16
+              MFMA peak: achieved = 2*A*H*F flop per launch / its mean duration
+              from HIP events the library records on its own stream
+cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s and FFN TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU work for the oracle sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_21_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, per_launch_units: int):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel sources and the same workload."""
+    try:
+        with open(PMC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    if not k or k.get("rows") != per_launch_units:
+        return None
+    return k.get("hbm_bytes")
+
+
+def cpu_baseline(spec, inp, target_s: float):
+    """Time the fp64 oracle on the host: routing + dispatch over all T tokens,
+    the expert FFN + combine on a contiguous token prefix sized to ~target_s of
+    work, scaled linearly to T (the FFN is per token)."""
+    import numpy as np
+    import oracle as om
+    t0 = time.perf_counter()
+    lg = om.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    r = om.route(spec, lg)
+    dsp = om.dispatch(spec, r["topk_idx"])
+    t_route = time.perf_counter() - t0
+
+    def ffn(n):
+        t1 = time.perf_counter()
+        om.forward_tokens(spec, inp["x"], r["topk_idx"], r["topk_w"], dsp["pos"], inp["W1"],
+                          inp.get("b1"), inp["W2"], inp.get("b2"), np.arange(n))
+        return time.perf_counter() - t1
+
+    threads = om.num_threads()
+    n0 = min(spec.T, max(threads, 8))
+    t_probe = ffn(n0)
+    n = int(min(spec.T, max(n0, n0 * max(target_s - t_route, 1.0) / max(t_probe, 1e-6))))
+    t_ffn = ffn(n) if n > n0 else t_probe
+    per_tok = t_ffn / n
+    total = t_route + per_tok * spec.T
+    return {"value": spec.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 C oracle, {threads} OpenMP threads: gate/softmax/top-k/losses/"
+                       f"dispatch over all {spec.T} tokens ({t_route:.2f} s) + expert FFN and "
+                       f"combine on tokens 0..{n - 1} ({t_ffn:.2f} s), FFN time scaled "
+                       f"linearly to {spec.T} tokens")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_mixture_experts_21_amd as moe
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    moe.lib()
+
+    spec = W.CONFIGS[args.config]
+    T, H, E, k, F = spec.T, spec.H, spec.E, spec.k, spec.F
+    log(f"[bench] generating {spec.name}")
+    t0 = time.perf_counter()
+    inp = W.generate(spec)
+    log(f"[bench] inputs drawn in {time.perf_counter() - t0:.1f} s")
+
+    sd = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if a is None:
+            return None
+        if spec.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {kk: dev(v) for kk, v in inp.items()}
+    prob = moe.Problem.from_spec(spec)
+    ws = torch.empty(moe.moe_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, H, dtype=sd, device="cuda")
+    losses = torch.empty(2, dtype=torch.float32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    evs = [moe.StageEvents() for _ in range(args.steps)]
+
+    def step(ev=None):
+        moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], out,
+                        losses, ws, offsets=offsets, events=ev)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    stage = np.array([ev.stage_ms() for ev in evs])          # [steps][5]
+    stage_mean = stage.mean(axis=0)
+    A = int(offsets[-1].item())
+    names = moe.STAGE_NAMES
+    sm = {n: float(v) for n, v in zip(names, stage_mean)}
+    gemm_flops = 2.0 * A * H * F                              # per GEMM launch
+    ffn_ms = sm["ffn_up"] + sm["ffn_down"]
+    ffn_tflops = 2 * gemm_flops / (ffn_ms * 1e-3) / 1e12
+    dom = "ffn_up" if sm["ffn_up"] >= sm["ffn_down"] else "ffn_down"
+    achieved = gemm_flops / (sm[dom] * 1e-3) / 1e12
+    s = spec.elem_bytes
+    alg_bytes = {
+        "route": T * H * s + H * E * s + T * k * 8,
+        "permute": T * k * 4 + 2 * A * 4,            # gather fused into ffn_up in moe_forward
+        "combine": A * H * s + T * k * 8 + T * H * s,
+    }
+    hbm = {n: {"ms": sm[n], "GB/s": alg_bytes[n] / (sm[n] * 1e-3) / 1e9,
+               "frac": alg_bytes[n] / (sm[n] * 1e-3) / 1e9 / PEAK_HBM_GBS} for n in alg_bytes}
+    kern = "ffn_gemm_bf16_up" if dom == "ffn_up" else "ffn_gemm_bf16_down"
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": spec.name, "T": T, "H": H, "E": E, "k": k, "F": F,
+                   "capacity_factor": spec.cf, "kept_rows": A},
+        "roofline": {"bound": "mfma", "kernel": kern, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_for(kern, A)},
+        "ffn_tflops": ffn_tflops,
+        "ffn_frac_of_bf16_peak": ffn_tflops / PEAK_BF16_TFLOPS,
+        "stage_ms": sm,
+        "hbm_stages": hbm,
+        "losses": [float(v) for v in losses.cpu().numpy()],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse top-k Mixture-of-Experts FFN
+ * forward.
+ *
+ * The layer is the one described by the "moe-training" SKILL page (Quick
+ * Start, Basic MoE Architecture): a gate linear over the hidden state, softmax
+ * over experts, top-k selection, renormalisation of the k selected scores to
+ * sum to 1, a per-expert Linear(H,F) -> GELU -> Linear(F,H) network (F = 4H on
+ * that page), and a weighted sum of the selected experts' outputs.  The router
+ * also yields the load-balancing loss E * sum_e f_e * P_e and the router
+ * z-loss mean(logsumexp(logits)^2) (Core Concepts, 3. Load Balancing), and
+ * dispatch honours an expert capacity derived from a capacity factor
+ * (Core Concepts, 4. Expert Parallelism: capacity_factor, drop_tokens).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *   buffer; the library never allocates, frees, or keeps a pointer after a
+ *   call returns, and holds no state, so calls on distinct streams with
+ *   distinct workspaces may run concurrently.
+ * - Every GPU call is asynchronous on `stream` and never synchronises with
+ *   the host, so a call sequence can be captured into a HIP graph.
+ * - Row-major storage.  x[T][H]; gate Wg[H][E]; W1[E][H][F]; W2[E][F][H]:
+ *   weights are stored [in][out] (the transpose of nn.Linear's [out][in]).
+ *   Biases bg[E], b1[E][F], b2[E][H] may be NULL (zero bias).
+ * - `dtype` is the storage type of x, weights, biases and of xp, h, y, out.
+ *   Arithmetic accumulates in fp32 for both.  logits and topk_w are fp32,
+ *   indices int32.
+ * - Every argument is validated on the host BEFORE anything is enqueued; on
+ *   error nothing is launched and a status other than MOE_OK is returned.
+ *   Device faults are asynchronous and surface at the caller's next
+ *   synchronisation, as with any stream API.  No C++ exception crosses the ABI.
+ * - Kernel envelope: 1 <= E <= 256, 1 <= k <= min(E, 8), T * k < 2^31,
+ *   H and F multiples of 8 (bf16) or 4 (fp32), every pointer 16-byte aligned.
+ *   Outside it a call returns MOE_ERR_UNSUPPORTED.
+ *
+ * Determinism: no floating-point atomics are used; repeated calls on the same
+ * inputs produce bitwise-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* null required pointer, T<1, E<1, k<1, k>E, H<1, F<1, bad dtype */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid, but outside the kernel envelope above */
+    MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the call needs */
+    MOE_ERR_HIP = 4           /* a HIP launch or event call failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+typedef struct {
+    int64_t T;               /* tokens (batch * sequence, flattened) */
+    int32_t H;               /* hidden width */
+    int32_t E;               /* number of experts */
+    int32_t k;               /* experts chosen per token */
+    int32_t F;               /* expert inner width (4H on the pages) */
+    double capacity_factor;  /* <= 0: no capacity limit (capacity = T) */
+    int32_t dtype;           /* moe_dtype_t */
+    int32_t reserved;        /* must be 0 */
+} moe_problem_t;
+
+/* moe_route flag: read `logits` as an input and skip the gate linear. */
+#define MOE_ROUTE_LOGITS_IN 1u
+
+/* Events recorded by moe_forward when `stage_events` is non-NULL: event i is
+ * recorded on `stream` just before stage i starts, the last one after the
+ * final stage.  The FFN up and down stages are one kernel launch each. */
+enum {
+    MOE_EV_ROUTE = 0,
+    MOE_EV_PERMUTE = 1,
+    MOE_EV_FFN_UP = 2,
+    MOE_EV_FFN_DOWN = 3,
+    MOE_EV_COMBINE = 4,
+    MOE_EV_END = 5,
+    MOE_FORWARD_EVENTS = 6
+};
+
+/* Expert capacity (host, synchronous): T when capacity_factor <= 0, else
+ * ceil(capacity_factor * T * k / E) evaluated in double.  The capacity
+ * follows the DeepSpeed MoE config on the "moe-training" SKILL page (Core
+ * Concepts, 4. Expert Parallelism): the batch's routed load, scaled by the
+ * capacity factor and shared evenly among the experts; here the load counts
+ * all k selections of every token. */
+moe_status_t moe_capacity(const moe_problem_t* p, int64_t* cap /* host */);
+
+/* Workspace bytes (host, synchronous) that suffice for EVERY call below on
+ * this problem, including moe_forward with all its optional outputs NULL. */
+moe_status_t moe_workspace_bytes(const moe_problem_t* p, size_t* bytes /* host */);
+
+/* Router: gate linear, softmax, top-k and renormalisation of the reference
+ * layer (Quick Start, Basic MoE Architecture), plus the two router losses of
+ * Core Concepts, 3. Load Balancing.
+ *   logits[T][E]   fp32; gate output x.Wg + bg.  Optional output (NULL to
+ *                  skip); with MOE_ROUTE_LOGITS_IN it is a required input.
+ *   topk_idx[T][k] int32; the k largest logits of each token in descending
+ *                  order, equal logits taken lower expert index first.
+ *   topk_w[T][k]   fp32; softmax probabilities of the chosen experts divided
+ *                  by their sum (they sum to 1; w == 1 when k == 1).
+ *   counts[E]      int32; how many (token, slot) pairs chose each expert,
+ *                  before capacity.
+ *   losses[2]      fp32; {aux, z}: aux = E * sum_e (counts_e / (T k)) *
+ *                  mean_t softmax_e, z = mean_t logsumexp_t^2.  Raw values,
+ *                  no loss coefficients applied. */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* Wg,
+                       const void* bg, float* logits, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, float* losses, uint32_t flags, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch with capacity dropping (the reference layer's per-expert token
+ * gather, Quick Start, Basic MoE Architecture, with the capacity and token
+ * dropping of the DeepSpeed config in Core Concepts, 4): per expert,
+ * the first `capacity` (token, slot) pairs in ascending token order are kept,
+ * the rest dropped.  Kept rows are laid out expert-major, token-ascending
+ * within an expert.
+ *   offsets[E+1]   int32; expert e owns rows [offsets[e], offsets[e+1]);
+ *                  A = offsets[E] rows are kept in total.
+ *   pos[T][k]      int32; row of the pair in xp, or -1 if dropped.
+ *   row_token[T*k] int32; token of each kept row (rows >= A are unspecified).
+ *   xp[T*k][H]     gathered copies of x rows (rows >= A are unspecified). */
+moe_status_t moe_permute(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                         int32_t* offsets, int32_t* pos, int32_t* row_token, void* xp,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFN (Quick Start, Basic MoE Architecture: Linear(H, F) -> GELU ->
+ * Linear(F, H) per expert) on the
+ * rows of each expert, as one grouped GEMM pair over unequal groups:
+ *   h[r] = GELU(xp[r] . W1[e] + b1[e])   with exact GELU 0.5 a (1 + erf(a/sqrt2)),
+ *   y[r] = h[r] . W2[e] + b2[e]          for offsets[e] <= r < offsets[e+1].
+ * h[T*k][F] and y[T*k][H] are written for rows < offsets[E] only. */
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_t* offsets,
+                            const void* W1, const void* b1, const void* W2, const void* b2,
+                            void* h, void* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine (Quick Start, Basic MoE Architecture): for every token
+ *   out[t] = sum over s = 0..k-1 with pos[t][s] >= 0 of topk_w[t][s] * y[pos[t][s]],
+ * accumulated in fp32 in slot order and rounded once; a token whose slots
+ * were all dropped gets a zero row.  Every row of out[T][H] is written. */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* pos,
+                         const float* topk_w, void* out, hipStream_t stream);
+
+/* The whole layer: route -> permute -> expert FFN -> combine, with results
+ * identical to calling the stages in sequence.  out[T][H] and losses[2] are
+ * required; logits, topk_idx, topk_w, counts, offsets and pos are optional
+ * outputs (NULL keeps them in the workspace).  stage_events is NULL or an
+ * array of MOE_FORWARD_EVENTS created events (see above). */
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg,
+                         const void* bg, const void* W1, const void* b1, const void* W2,
+                         const void* b2, void* out, float* losses, float* logits,
+                         int32_t* topk_idx, float* topk_w, int32_t* counts,
+                         int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t* stage_events);
+
+/* Static description of a status code (host). */
+const char* moe_status_string(moe_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

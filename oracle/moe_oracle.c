@@ -62,7 +62,7 @@ int orc_num_threads(void) {
 #endif
 }
 
-/* Gate linear: l = x . Wg + bg  ("Compute gate scores", Basic MoE Architecture). */
+/* Gate linear: l = x . Wg + bg  (Quick Start, Basic MoE Architecture). */
 int orc_logits(const orc_problem* p, const void* x, const void* Wg, const void* bg,
                double* logits) {
     if (!valid(p) || !x || !Wg || !logits) return -1;
@@ -84,8 +84,7 @@ int orc_logits(const orc_problem* p, const void* x, const void* Wg, const void* 
 
 /* Softmax over experts, top-k, renormalisation of the k scores, expert counts,
  * the load-balancing loss E * sum_e f_e P_e and the z-loss mean(lse^2)
- * (Basic MoE Architecture: "Top-k routing", "Normalize top-k scores";
- * 3. Load Balancing: auxiliary loss and router z-loss). */
+ * (Quick Start, Basic MoE Architecture; Core Concepts, 3. Load Balancing). */
 int orc_route(const orc_problem* p, const double* logits, int32_t* topk_idx,
               double* topk_w, double* probs, double* lse, int32_t* counts, double* aux,
               double* z) {
@@ -260,7 +259,7 @@ int orc_expert_rows(const orc_problem* p, const void* rows, int64_t n,
 }
 
 /* Weighted sum over the k slots, in slot order, starting from zero
- * ("Dispatch and combine expert outputs", Basic MoE Architecture).  A dropped
+ * (Quick Start, Basic MoE Architecture).  A dropped
  * slot contributes nothing and the other weights are not renormalised. */
 int orc_forward_tokens(const orc_problem* p, const void* x, const int32_t* topk_idx,
                        const double* topk_w, const int32_t* pos, const void* W1,

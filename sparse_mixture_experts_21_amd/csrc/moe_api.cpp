@@ -1,0 +1,228 @@
+// C ABI of libmoe.so: argument validation, capacity, workspace layout and the
+// launch sequence of every stage.  All validation happens before the first
+// HIP call, so a rejected call enqueues nothing (and needs no GPU).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const moe_problem_t& p) {
+    WsLayout L;
+    std::memset(&L, 0, sizeof L);
+    const size_t T = (size_t)p.T, H = (size_t)p.H, E = (size_t)p.E, k = (size_t)p.k,
+                 F = (size_t)p.F;
+    const size_t s = p.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    L.nblk_route = (p.T + kRouteTok - 1) / kRouteTok;
+    L.nchunk = (p.T + kChunkTok - 1) / kChunkTok;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t nb = (size_t)L.nblk_route, nc = (size_t)L.nchunk;
+    L.wgt = take(p.dtype == MOE_DTYPE_BF16 ? E * H * 2 : 0);
+    L.blk_psum = take(nb * E * 4);
+    L.blk_lse2 = take(nb * 4);
+    L.blk_cnt = take(nb * E * 4);
+    L.fin = take((E + 1) * 8);
+    L.route_bytes = off;
+    L.chunk_hist = take(nc * E * 4);
+    L.chunk_base = take(nc * E * 4);
+    L.misc = take(256);
+    L.permute_bytes = off;
+    L.ffn_bytes = 0;
+    L.logits = 0;                 // moe_forward never stores logits in the workspace
+    L.topk_idx = take(T * k * 4);
+    L.topk_w = take(T * k * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.pos = take(T * k * 4);
+    L.row_token = take(T * k * 4);
+    L.xp = 0;                     // moe_forward gathers x inside the first GEMM
+    L.h = take(T * k * F * s);
+    L.y = take(T * k * H * s);
+    L.total = off;
+    return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool opt_ok(const void* ptr) { return ptr == nullptr || aligned16(ptr); }
+
+moe_status_t check_problem(const moe_problem_t* p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 1 || p->H < 1 || p->F < 1 || p->E < 1 || p->k < 1 || p->k > p->E)
+        return MOE_ERR_INVALID_ARG;
+    if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (p->reserved != 0) return MOE_ERR_INVALID_ARG;
+    if (std::isnan(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+    if (p->E > kMaxE || p->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+    if (p->T > (int64_t)0x7fffffff / p->k) return MOE_ERR_UNSUPPORTED;
+    const int vec = p->dtype == MOE_DTYPE_BF16 ? 8 : 4;
+    if (p->H % vec != 0 || p->F % vec != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int64_t capacity_of(const moe_problem_t& p) {
+    if (!(p.capacity_factor > 0.0)) return p.T;
+    const double c = std::ceil(p.capacity_factor * (double)(p.T * (int64_t)p.k) / (double)p.E);
+    if (c >= 9.0e18) return INT64_MAX;
+    return (int64_t)c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported problem (outside the kernel envelope)";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch or event failure";
+    }
+    return "unknown status";
+}
+
+moe_status_t moe_capacity(const moe_problem_t* p, int64_t* cap) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!cap) return MOE_ERR_INVALID_ARG;
+    *cap = capacity_of(*p);
+    return MOE_OK;
+}
+
+moe_status_t moe_workspace_bytes(const moe_problem_t* p, size_t* bytes) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = ws_layout(*p).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* Wg, const void* bg,
+                       float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       float* losses, uint32_t flags, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+    const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+    if (!topk_idx || !topk_w || !counts || !losses || !ws) return MOE_ERR_INVALID_ARG;
+    if (logits_in ? !logits : (!x || !Wg)) return MOE_ERR_INVALID_ARG;
+    if (!opt_ok(x) || !opt_ok(Wg) || !opt_ok(bg) || !opt_ok(logits) || !aligned16(topk_idx) ||
+        !aligned16(topk_w) || !aligned16(counts) || !aligned16(losses) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(*p);
+    if (ws_bytes < L.route_bytes) return MOE_ERR_WORKSPACE;
+    hipError_t e = launch_route(*p, L, static_cast<char*>(ws), x, Wg, bg, logits, logits_in,
+                                topk_idx, topk_w, counts, losses, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_permute(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                         int32_t* offsets, int32_t* pos, int32_t* row_token, void* xp, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!x || !topk_idx || !offsets || !pos || !row_token || !xp || !ws)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(offsets) || !aligned16(pos) ||
+        !aligned16(row_token) || !aligned16(xp) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(*p);
+    if (ws_bytes < L.permute_bytes) return MOE_ERR_WORKSPACE;
+    hipError_t e = launch_permute(*p, L, static_cast<char*>(ws), capacity_of(*p), x, topk_idx,
+                                  offsets, pos, row_token, xp, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_t* offsets,
+                            const void* W1, const void* b1, const void* W2, const void* b2,
+                            void* h, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!xp || !offsets || !W1 || !W2 || !h || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(xp) || !aligned16(offsets) || !aligned16(W1) || !opt_ok(b1) ||
+        !aligned16(W2) || !opt_ok(b2) || !aligned16(h) || !aligned16(y))
+        return MOE_ERR_UNSUPPORTED;
+    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, stream);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const void* y, const int32_t* pos,
+                         const float* topk_w, void* out, hipStream_t stream) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!y || !pos || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(pos) || !aligned16(topk_w) || !aligned16(out))
+        return MOE_ERR_UNSUPPORTED;
+    hipError_t e = launch_combine(*p, y, pos, topk_w, out, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, const void* bg,
+                         const void* W1, const void* b1, const void* W2, const void* b2,
+                         void* out, float* losses, float* logits, int32_t* topk_idx,
+                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* pos,
+                         void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipEvent_t* stage_events) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!x || !Wg || !W1 || !W2 || !out || !losses || !ws) return MOE_ERR_INVALID_ARG;
+    if (stage_events) {
+        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    }
+    if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
+        !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !aligned16(losses) ||
+        !opt_ok(logits) || !opt_ok(topk_idx) || !opt_ok(topk_w) || !opt_ok(counts) ||
+        !opt_ok(offsets) || !opt_ok(pos) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(*p);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + L.topk_idx);
+    float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.topk_w);
+    int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(w + L.counts);
+    int32_t* off = offsets ? offsets : reinterpret_cast<int32_t*>(w + L.offsets);
+    int32_t* ps = pos ? pos : reinterpret_cast<int32_t*>(w + L.pos);
+    int32_t* rt = reinterpret_cast<int32_t*>(w + L.row_token);
+    void* h = w + L.h;
+    void* y = w + L.y;
+
+    auto ev = [&](int i) -> hipError_t {
+        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+    };
+    hipError_t e = ev(MOE_EV_ROUTE);
+    if (e == hipSuccess)
+        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
+    if (e == hipSuccess)
+        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
+    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
+    if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_END);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations shared by the HIP sources of libmoe.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- types
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+// bf16 <-> fp32 on raw 16-bit patterns.  Widening is exact; narrowing rounds to
+// nearest even (inputs here are finite).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- workspace
+// Byte offsets of every scratch region inside the caller's workspace; all
+// regions are 256-byte aligned.  Regions a call does not use are still laid
+// out so that one layout serves every entry point.
+struct WsLayout {
+    size_t wgt;          // gate weights transposed to [E][H] (bf16 router)
+    size_t blk_psum;     // [nblk_route][E] fp32: per-block sums of softmax probs
+    size_t blk_lse2;     // [nblk_route]    fp32: per-block sums of lse^2
+    size_t blk_cnt;      // [nblk_route][E] int32: per-block expert histograms
+    size_t fin;          // finalize scratch: [E] double + ticket
+    size_t chunk_hist;   // [nchunk][E] int32
+    size_t chunk_base;   // [nchunk][E] int32
+    size_t misc;         // small scalars (kept rows total, ...)
+    // moe_forward intermediates, used when the caller passes NULL
+    size_t logits, topk_idx, topk_w, counts, offsets, pos, row_token, xp, h, y;
+    size_t route_bytes, permute_bytes, ffn_bytes, total;
+    int64_t nblk_route, nchunk;
+};
+
+constexpr int kRouteTok = 16;      // tokens per router workgroup
+constexpr int kChunkTok = 128;     // tokens per dispatch chunk
+
+WsLayout ws_layout(const moe_problem_t& p);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; none synchronises.
+hipError_t launch_route(const moe_problem_t& p, const WsLayout& L, char* ws, const void* x,
+                        const void* Wg, const void* bg, float* logits, bool logits_in,
+                        int32_t* topk_idx, float* topk_w, int32_t* counts, float* losses,
+                        hipStream_t s);
+hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, int64_t cap,
+                          const void* x, const int32_t* topk_idx, int32_t* offsets,
+                          int32_t* pos, int32_t* row_token, void* xp, hipStream_t s);
+// rowmap (nullable): when set, row r of the first GEMM reads x[rowmap[r]]
+// instead of xp[r] (the gather fused into the operand load).
+hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
+                         const int32_t* offsets, const void* W1, const void* b1, void* h,
+                         hipStream_t s);
+hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
+                           const void* W2, const void* b2, void* y, hipStream_t s);
+hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
+                          const float* topk_w, void* out, hipStream_t s);
+
+}  // namespace moe
