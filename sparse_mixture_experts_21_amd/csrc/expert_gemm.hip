@@ -14,14 +14,15 @@
 // with no rows cost nothing (their weights are never read).
 //
 // bf16 kernel (gfx950): 256 threads, tile BN = 256 output columns x BM rows,
-// BK = 64, v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The MFMA is
-// issued as D[n][m] = W^T[n][k] . X^T[k][m], so both LDS tiles are stored
-// K-contiguous ([n][k] and [m][k], 128-byte rows, 16-byte chunks XOR-swizzled
-// by row to spread banks) and each lane of the epilogue owns 4 consecutive
-// output columns -> 8-byte stores.  The weights arrive [k][n] (N-contiguous):
-// each thread loads an 8 x 8 block (8 rows of 16 bytes), transposes it in
-// registers and writes 8 K-contiguous 16-byte chunks.  Two LDS stages: the
-// global loads of tile k+1 are in flight while tile k is multiplied.
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, issued as
+// D[n][m] = W^T[n][k] . X^T[k][m] so each lane of the epilogue owns 4
+// consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
+// buffer_load ... lds (no VGPR staging) through 4 LDS stages of a 32-deep
+// k-tile, issued 3 k-tiles ahead of the MFMAs.  The weights stay in their
+// natural [k][n] layout in LDS and are turned into K-contiguous MFMA
+// fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
+// fragment reads for the next k-substep are interleaved with the MFMAs of
+// the current one, and one barrier per k-tile orders DMA and reads.
 #include "moe_internal.h"
 
 namespace moe {
@@ -57,85 +58,177 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 // ---------------------------------------------------------------- bf16 MFMA
 template <int BM>
 struct Cfg {
-    static constexpr int BN = 256, BK = 64;
+    static constexpr int BN = 256, BK = 32, NS = 4;  // 4 LDS stages of a 32-deep k-tile
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
     static constexpr int FN = TN / 32, FM = TM / 32; // 32x32 MFMA tiles per wave
-    static constexpr int XCH = BM * 8 / 256;         // X 16-byte chunks per thread per k-tile
-    static constexpr int STAGE = (BN + BM) * BK;     // bf16 elements per LDS stage
+    static constexpr int W_BYTES = BK * BN * 2;      // weight tile [BK][BN], 512-byte rows
+    static constexpr int X_BYTES = BM * BK * 2;      // row tile [BM][BK], 64-byte rows
+    static constexpr int STAGE = W_BYTES + X_BYTES;
+    static constexpr int WI = W_BYTES / 4096;        // 1 KB DMA blocks per wave (weights)
+    static constexpr int XI = X_BYTES / 4096;        // 1 KB DMA blocks per wave (rows)
+    static constexpr int GM = 8;                     // m-tiles per tile group (L2 reuse)
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)) << 3; }
+// Raw buffer resource: accesses at byte offsets >= num_records return zero
+// without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 
+constexpr uint32_t kOob = 0x80000000u;   // an offset beyond every resource's range
+
+// 16 bytes per lane from global memory straight into LDS (M0 + 16 * lane);
+// no VGPR is written, so nothing is left in flight in registers.  Completion
+// is tracked with vmcnt by the caller.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding; lgkmcnt and expcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
+// Workgroup -> (row tile, column tile).  The hardware deals workgroups to the
+// 8 XCDs round-robin; remap so that each XCD walks a contiguous range of the
+// logical order, and order that range in groups of GM row tiles x all column
+// tiles so the ~32 tiles an XCD runs at once share X and W slices in its L2.
+__device__ __forceinline__ void tile_coords(int b, int nblk, int Mt, int Nt, int GM, int& mt,
+                                            int& nt) {
+    const int x = b & 7, j = b >> 3;
+    const int q = nblk >> 3, r = nblk & 7;
+    const int lid = x * q + min(x, r) + j;
+    const int per_group = GM * Nt;
+    const int g = lid / per_group, w = lid % per_group;
+    const int m_base = g * GM;
+    const int gm = min(GM, Mt - m_base);
+    mt = m_base + w % gm;
+    nt = w / gm;
+}
+
+// LDS layouts (per stage):
+//   weights [k][n]: 32 rows of 512 bytes; 16-byte chunk c of row k is stored
+//     at chunk c ^ (4 (k & 3)).  A-fragments are read with ds_read_b64_tr_b16:
+//     in each 16-lane group, source lane s reads 4 consecutive n of row
+//     k0 + s/4 and lane i receives k0..k0+3 of column n0 + i, i.e. the
+//     K-contiguous operand the MFMA wants, from an N-contiguous tile.
+//   rows [m][k]: 64-byte rows; chunk c of row m is stored at c ^ ((m >> 2) & 3).
+// Both swizzles make every fragment read land in 16 distinct 16-byte bank
+// slots per 16 lanes; the DMA writes are 1 KB contiguous per instruction.
 template <int BM, int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16(
-    const uint16_t* __restrict__ X, const int32_t* __restrict__ rowmap,
+    const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt_max) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt, int Nt) {
     using G = Cfg<BM>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[G::NS * G::STAGE];
 
-    const int mt = blockIdx.x % Mt_max;
-    const int nt = blockIdx.x / Mt_max;
+    int mt, nt;
+    tile_coords(blockIdx.x, gridDim.x, Mt, Nt, G::GM, mt, nt);
     int e, m0, row_begin, n_rows;
     if (!find_tile<BM>(offsets, E, mt, e, m0, row_begin, n_rows)) return;
     const int n0 = nt * G::BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-    // ---- per-thread global source addresses
-    const uint16_t* xsrc[G::XCH];
-    int xrow[G::XCH], xchk[G::XCH];
+    // ---- DMA sources (byte offsets; fixed for the whole k loop except + k0)
+    const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(X, x_bytes);
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        make_rsrc(W + (int64_t)e * K * N, (uint32_t)K * (uint32_t)N * 2u);
+    uint32_t woff[G::WI];
 #pragma unroll
-    for (int i = 0; i < G::XCH; ++i) {
-        const int lin = tid + 256 * i;
-        xrow[i] = lin >> 3;
-        xchk[i] = lin & 7;
-        const int r = row_begin + min(m0 + xrow[i], n_rows - 1);
-        const int64_t src = rowmap ? (int64_t)rowmap[r] : (int64_t)r;
-        xsrc[i] = X + src * K + xchk[i] * 8;
+    for (int q = 0; q < G::WI; ++q) {
+        const int blk = 4 * q + wave;                       // 1 KB block = 2 weight rows
+        const int k = 2 * blk + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * (k & 3));           // logical 16-byte chunk
+        woff[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)(n0 + 8 * c) * 2u;
     }
-    const int kb = tid >> 5, nb = tid & 31;            // this thread's 8x8 weight block
-    const bool wcol_ok = (n0 + nb * 8) < N;
-    const uint16_t* wsrc = W + (int64_t)e * K * N + (int64_t)(kb * 8) * N + n0 + nb * 8;
-
-    u32x4_t xr[G::XCH];
-    u32x4_t wr[8];
-
-    auto load_tile = [&](int k0) {
+    uint32_t xoff[G::XI];
+    int xk[G::XI];
 #pragma unroll
-        for (int i = 0; i < G::XCH; ++i) {
-            xr[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (k0 + xchk[i] * 8 < K) xr[i] = *reinterpret_cast<const u32x4_t*>(xsrc[i] + k0);
-        }
+    for (int q = 0; q < G::XI; ++q) {
+        const int blk = 4 * q + wave;                       // 1 KB block = 16 rows
+        const int row = 16 * blk + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int r = row_begin + min(m0 + row, n_rows - 1);
+        const uint32_t src = rowmap ? (uint32_t)rowmap[r] : (uint32_t)r;
+        xoff[q] = src * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        xk[q] = 8 * c;
+    }
+    const uint32_t wstep = (uint32_t)G::BK * (uint32_t)N * 2u;
+
+    auto issue_tile = [&](int t) {                          // k-tile t -> stage t % NS
+        const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
+        const int k0 = t * G::BK;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            wr[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (wcol_ok && k0 + kb * 8 + i < K)
-                wr[i] = *reinterpret_cast<const u32x4_t*>(wsrc + (int64_t)(k0 + i) * N);
+        for (int q = 0; q < G::WI; ++q)
+            dma16(w_rsrc, woff[q] + (uint32_t)t * wstep,
+                  __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024)));
+#pragma unroll
+        for (int q = 0; q < G::XI; ++q) {
+            const uint32_t o = (k0 + xk[q] < K) ? xoff[q] + (uint32_t)k0 * 2u : kOob;
+            dma16(x_rsrc, o,
+                  __builtin_amdgcn_readfirstlane(st + (uint32_t)(G::W_BYTES + (4 * q + wave) * 1024)));
         }
     };
-    auto store_tile = [&](int stage) {
-        uint16_t* ws_ = lds + stage * G::STAGE;            // [BN][BK]
-        uint16_t* xs_ = ws_ + G::BN * G::BK;               // [BM][BK]
+
+    // ---- fragment read addresses (bytes, relative to a stage base)
+    const int l32 = lane & 31, half = lane >> 5;
+    uint32_t aoff[G::FN], boff[G::FM];
+    {
+        const int grp = lane >> 4, s16 = lane & 15;
+        const int k = 8 * (grp >> 1) + (s16 >> 2);          // + 16 kk, + 4 for the 2nd read
 #pragma unroll
-        for (int i = 0; i < G::XCH; ++i)
-            *reinterpret_cast<u32x4_t*>(xs_ + xrow[i] * G::BK + swz(xrow[i], xchk[i])) = xr[i];
-        // 8x8 transpose: column j of the block = k values kb*8..kb*8+7 of n = nb*8 + j
+        for (int i = 0; i < G::FN; ++i) {
+            const int n = wn * G::TN + 32 * i + 16 * (grp & 1) + 4 * (s16 & 3);
+            const int pc = (n >> 3) ^ (4 * (k & 3));
+            aoff[i] = (uint32_t)(k * 512 + pc * 16 + (n & 4) * 2);
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int d = j >> 1;
-            u32x4_t o;
+        for (int j = 0; j < G::FM; ++j) {
+            const int m = wm * G::TM + 32 * j + l32;
+            boff[j] = (uint32_t)(m * 64);                    // + chunk, swizzled per kk
+        }
+    }
+    bf16x8_t fa[2][G::FN], fb[2][G::FM];
+    auto read_frags = [&](int t, int kk, int buf) {
+        const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = wr[2 * q][d], hi = wr[2 * q + 1][d];
-                o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                               : ((lo & 0xffffu) | (hi << 16));
-            }
-            const int n = nb * 8 + j;
-            *reinterpret_cast<u32x4_t*>(ws_ + n * G::BK + swz(n, kb)) = o;
+        for (int i = 0; i < G::FN; ++i) {
+            const uint32_t a = st + aoff[i] + (uint32_t)(kk * 16 * 512);
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16_t*)(uintptr_t)a);
+            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16_t*)(uintptr_t)(a + 4 * 512));
+            const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            fa[buf][i] = __builtin_bit_cast(bf16x8_t, v);
+        }
+#pragma unroll
+        for (int j = 0; j < G::FM; ++j) {
+            const int m = wm * G::TM + 32 * j + l32;
+            const int pc = (2 * kk + half) ^ ((m >> 2) & 3);
+            const uint32_t b = st + G::W_BYTES + boff[j] + (uint32_t)(pc * 16);
+            fb[buf][j] = *(const lds_bf16x8_t*)(uintptr_t)b;
         }
     };
 
@@ -146,42 +239,54 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         for (int j = 0; j < G::FM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < G::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < G::FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
+                                                                    acc[i][j], 0, 0, 0);
+    };
+    constexpr int NMF = G::FN * G::FM;
+    constexpr int NRD = 2 * G::FN + G::FM;   // LDS read instructions per substep
+    constexpr int NDMA = G::WI + G::XI;      // DMA instructions per wave per k-tile
 
+    // ---- pipeline: DMA runs NS-1 k-tiles ahead of the MFMAs
     const int nk = (K + G::BK - 1) / G::BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < G::NS; ++t) issue_tile(t);
+    wait_vmcnt<(G::NS - 1) * NDMA>();
+    lds_barrier();
+    read_frags(0, 0, 0);
 
-    const int half = lane >> 5, l32 = lane & 31;
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tile((kt + 1) * G::BK);
-        const uint16_t* ws_ = lds + cur * G::STAGE;
-        const uint16_t* xs_ = ws_ + G::BN * G::BK;
+        // substep 0: MFMAs on k 0..15 while reading k 16..31 of this tile
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(kt, 1, 1);
+        mfma(0);
 #pragma unroll
-        for (int kk = 0; kk < G::BK / 16; ++kk) {
-            const int chunk = 2 * kk + half;
-            bf16x8_t a[G::FN], b[G::FM];
-#pragma unroll
-            for (int i = 0; i < G::FN; ++i) {
-                const int n = wn * G::TN + 32 * i + l32;
-                a[i] = *reinterpret_cast<const bf16x8_t*>(ws_ + n * G::BK + swz(n, chunk));
-            }
-#pragma unroll
-            for (int j = 0; j < G::FM; ++j) {
-                const int m = wm * G::TM + 32 * j + l32;
-                b[j] = *reinterpret_cast<const bf16x8_t*>(xs_ + m * G::BK + swz(m, chunk));
-            }
-#pragma unroll
-            for (int i = 0; i < G::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < G::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j],
-                                                                        0, 0, 0);
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if (kt + 1 < nk) store_tile(cur ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // tile kt+1 complete in every wave's view; nobody reads stage kt % NS any more
+        wait_vmcnt<(G::NS - 2) * NDMA>();
+        wait_lgkm0();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // substep 1: refill this stage with tile kt+NS, first fragments of tile kt+1
+        issue_tile(kt + G::NS);
+        read_frags(kt + 1, 0, 0);
+        mfma(1);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
 
     // ---- epilogue: D[n][m]; lane owns m = l32 and n = 8 g + 4 half + 0..3
     const uint16_t* be = bias ? bias + (int64_t)e * N : nullptr;
@@ -310,12 +415,15 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         auto* w = static_cast<const uint16_t*>(W);
         auto* b = static_cast<const uint16_t*>(bias);
         auto* c = static_cast<uint16_t*>(Cout);
+        // bytes addressable through X: the token rows (gather) or the kept rows
+        const int64_t xrows = rowmap ? p.T : rows;
+        const uint32_t xb = (uint32_t)(xrows * K * 2);
         if (bm == 256)
-            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, rowmap, offsets, p.E, w, b, c, K, N, Mt);
+            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
         else if (bm == 128)
-            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, rowmap, offsets, p.E, w, b, c, K, N, Mt);
+            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
         else
-            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, rowmap, offsets, p.E, w, b, c, K, N, Mt);
+            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
         const int Nt = (N + 63) / 64;
