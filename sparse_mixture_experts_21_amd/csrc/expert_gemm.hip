@@ -30,8 +30,21 @@ namespace {
 
 enum Act { kActNone = 0, kActGelu = 1 };
 
+// Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)), with erf evaluated by formula
+// 7.1.26 of Abramowitz & Stegun, Handbook of Mathematical Functions:
+//   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
+//   t = 1 / (1 + p u), u >= 0, |error| <= 1.5e-7,
+// i.e. below fp32 rounding of GELU's output scale and far below bf16.  One
+// reciprocal and one exponential, no branches.
 __device__ __forceinline__ float gelu_erf(float a) {
-    return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
+    const float u = fabsf(a) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float q = t * poly * __expf(-u * u);          // 1 - erf(|a| / sqrt 2)
+    return 0.5f * a * ((a >= 0.0f) ? 2.0f - q : q);
 }
 
 // Locate the expert and row tile of row-tile index mt.  Returns false when mt
@@ -56,19 +69,34 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_NS
+#define MOE_GEMM_NS 4
+#endif
+#ifndef MOE_GEMM_GM
+#define MOE_GEMM_GM 8
+#endif
 template <int BM>
 struct Cfg {
-    static constexpr int BN = 256, BK = 32, NS = 4;  // 4 LDS stages of a 32-deep k-tile
+    static constexpr int BN = 256, BK = MOE_GEMM_BK;  // k-tile depth
+    static constexpr int NS = MOE_GEMM_NS;            // LDS stages (power of 2)
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
     static constexpr int FN = TN / 32, FM = TM / 32; // 32x32 MFMA tiles per wave
     static constexpr int W_BYTES = BK * BN * 2;      // weight tile [BK][BN], 512-byte rows
-    static constexpr int X_BYTES = BM * BK * 2;      // row tile [BM][BK], 64-byte rows
+    static constexpr int X_BYTES = BM * BK * 2;      // row tile [BM][BK], 2 BK-byte rows
+    static constexpr int CPR = BK / 8;               // 16-byte chunks per X row
+    static constexpr int RPB = 64 / CPR;             // X rows per 1 KB DMA block
+    static constexpr int RSH = (CPR == 4) ? 2 : 1;   // X swizzle: chunk ^= (m >> RSH) % CPR
     static constexpr int STAGE = W_BYTES + X_BYTES;
     static constexpr int WI = W_BYTES / 4096;        // 1 KB DMA blocks per wave (weights)
     static constexpr int XI = X_BYTES / 4096;        // 1 KB DMA blocks per wave (rows)
-    static constexpr int GM = 8;                     // m-tiles per tile group (L2 reuse)
+    static constexpr int GM = MOE_GEMM_GM;           // m-tiles per tile group (L2 reuse)
+    static_assert(BK == 32 || BK == 64, "k-tile depth");
+    static_assert((NS & (NS - 1)) == 0 && NS >= 2, "stages");
 };
 
 // Raw buffer resource: accesses at byte offsets >= num_records return zero
@@ -130,7 +158,8 @@ __device__ __forceinline__ void tile_coords(int b, int nblk, int Mt, int Nt, int
 //     in each 16-lane group, source lane s reads 4 consecutive n of row
 //     k0 + s/4 and lane i receives k0..k0+3 of column n0 + i, i.e. the
 //     K-contiguous operand the MFMA wants, from an N-contiguous tile.
-//   rows [m][k]: 64-byte rows; chunk c of row m is stored at c ^ ((m >> 2) & 3).
+//   rows [m][k]: rows of 2 BK bytes; chunk c of row m is stored at
+//     c ^ ((m >> RSH) % CPR), RSH = log2(16 / CPR).
 // Both swizzles make every fragment read land in 16 distinct 16-byte bank
 // slots per 16 lanes; the DMA writes are 1 KB contiguous per instruction.
 template <int BM, int ACT>
@@ -167,9 +196,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     int xk[G::XI];
 #pragma unroll
     for (int q = 0; q < G::XI; ++q) {
-        const int blk = 4 * q + wave;                       // 1 KB block = 16 rows
-        const int row = 16 * blk + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const int blk = 4 * q + wave;                       // 1 KB block = RPB rows
+        const int row = G::RPB * blk + lane / G::CPR;
+        const int c = (lane % G::CPR) ^ ((row >> G::RSH) % G::CPR);
         const int r = row_begin + min(m0 + row, n_rows - 1);
         const uint32_t src = rowmap ? (uint32_t)rowmap[r] : (uint32_t)r;
         xoff[q] = src * (uint32_t)K * 2u + (uint32_t)c * 16u;
@@ -177,18 +206,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     }
     const uint32_t wstep = (uint32_t)G::BK * (uint32_t)N * 2u;
 
-    auto issue_tile = [&](int t) {                          // k-tile t -> stage t % NS
+    // DMA number q (0 <= q < WI + XI) of k-tile t, into stage t % NS.  k-tiles
+    // past the end read at out-of-range offsets and fill the stage with zeros.
+    auto issue_one = [&](int t, int q) {
         const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
         const int k0 = t * G::BK;
-#pragma unroll
-        for (int q = 0; q < G::WI; ++q)
+        if (q < G::WI) {
             dma16(w_rsrc, woff[q] + (uint32_t)t * wstep,
                   __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024)));
-#pragma unroll
-        for (int q = 0; q < G::XI; ++q) {
-            const uint32_t o = (k0 + xk[q] < K) ? xoff[q] + (uint32_t)k0 * 2u : kOob;
+        } else {
+            const int qx = q - G::WI;
+            const uint32_t o = (k0 + xk[qx] < K) ? xoff[qx] + (uint32_t)k0 * 2u : kOob;
             dma16(x_rsrc, o,
-                  __builtin_amdgcn_readfirstlane(st + (uint32_t)(G::W_BYTES + (4 * q + wave) * 1024)));
+                  __builtin_amdgcn_readfirstlane(st + (uint32_t)(G::W_BYTES + (4 * qx + wave) * 1024)));
         }
     };
 
@@ -207,29 +237,33 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
 #pragma unroll
         for (int j = 0; j < G::FM; ++j) {
             const int m = wm * G::TM + 32 * j + l32;
-            boff[j] = (uint32_t)(m * 64);                    // + chunk, swizzled per kk
+            boff[j] = (uint32_t)(m * G::BK * 2);             // + chunk, swizzled per kk
         }
     }
     bf16x8_t fa[2][G::FN], fb[2][G::FM];
-    auto read_frags = [&](int t, int kk, int buf) {
+    // fragment f (f < FN: weights via two transposed reads; else rows) of
+    // k-substep kk of k-tile t into register buffer buf
+    auto read_frag = [&](int t, int kk, int buf, int f) {
         const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
-#pragma unroll
-        for (int i = 0; i < G::FN; ++i) {
-            const uint32_t a = st + aoff[i] + (uint32_t)(kk * 16 * 512);
+        if (f < G::FN) {
+            const uint32_t a = st + aoff[f] + (uint32_t)(kk * 16 * 512);
             const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_v4i16_t*)(uintptr_t)a);
             const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_v4i16_t*)(uintptr_t)(a + 4 * 512));
             const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            fa[buf][i] = __builtin_bit_cast(bf16x8_t, v);
-        }
-#pragma unroll
-        for (int j = 0; j < G::FM; ++j) {
+            fa[buf][f] = __builtin_bit_cast(bf16x8_t, v);
+        } else {
+            const int j = f - G::FN;
             const int m = wm * G::TM + 32 * j + l32;
-            const int pc = (2 * kk + half) ^ ((m >> 2) & 3);
+            const int pc = (2 * kk + half) ^ ((m >> G::RSH) % G::CPR);
             const uint32_t b = st + G::W_BYTES + boff[j] + (uint32_t)(pc * 16);
             fb[buf][j] = *(const lds_bf16x8_t*)(uintptr_t)b;
         }
+    };
+    auto read_frags = [&](int t, int kk, int buf) {
+#pragma unroll
+        for (int f = 0; f < G::FN + G::FM; ++f) read_frag(t, kk, buf, f);
     };
 
     f32x16_t acc[G::FN][G::FM];
@@ -239,50 +273,96 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         for (int j = 0; j < G::FM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    auto mfma = [&](int buf) {
+    // MFMAs number lo..hi-1 (row-major over the FN x FM accumulator tiles)
+    auto mfma_range = [&](int buf, int lo, int hi) {
 #pragma unroll
-        for (int i = 0; i < G::FN; ++i)
-#pragma unroll
-            for (int j = 0; j < G::FM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
-                                                                    acc[i][j], 0, 0, 0);
+        for (int x = 0; x < G::FN * G::FM; ++x) {
+            if (x < lo || x >= hi) continue;
+            const int i = x / G::FM, j = x % G::FM;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
+                                                                acc[i][j], 0, 0, 0);
+        }
     };
+    auto mfma = [&](int buf) { mfma_range(buf, 0, G::FN * G::FM); };
     constexpr int NMF = G::FN * G::FM;
     constexpr int NRD = 2 * G::FN + G::FM;   // LDS read instructions per substep
     constexpr int NDMA = G::WI + G::XI;      // DMA instructions per wave per k-tile
 
-    // ---- pipeline: DMA runs NS-1 k-tiles ahead of the MFMAs
+    // ---- pipeline: DMA runs NS-1 k-tiles ahead of the MFMAs.  The DMAs of a
+    // k-tile are spread over two substeps (H1 of them in the last substep of
+    // k-tile kt, after the barrier that frees their stage, the other H2 in the
+    // first substep of k-tile kt+1), one at a time between MFMAs, so the
+    // address units never see a burst that would stall the wave's issue.
+    constexpr int H1 = (NDMA + 1) / 2, H2 = NDMA - H1;
+    constexpr int NSUB = G::BK / 16;         // 16-deep MFMA k-substeps per k-tile
+    constexpr int NF = G::FN + G::FM;        // fragments per substep
     const int nk = (K + G::BK - 1) / G::BK;
 #pragma unroll
-    for (int t = 0; t < G::NS; ++t) issue_tile(t);
-    wait_vmcnt<(G::NS - 1) * NDMA>();
+    for (int t = 0; t + 1 < G::NS; ++t)
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q) issue_one(t, q);
+#pragma unroll
+    for (int q = 0; q < H1; ++q) issue_one(G::NS - 1, q);
+    wait_vmcnt<(G::NS - 2) * NDMA + H1>();
     lds_barrier();
     read_frags(0, 0, 0);
 
     for (int kt = 0; kt < nk; ++kt) {
-        // substep 0: MFMAs on k 0..15 while reading k 16..31 of this tile
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(kt, 1, 1);
-        mfma(0);
+        // substep 0: MFMAs of substep 0 || fragments of substep 1 || the rest
+        // of k-tile kt+NS-1's DMAs (its stage was freed one barrier ago)
 #pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int g = 0; g < H2; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(kt + G::NS - 1, H1 + g);
+            mfma_range(0, g * NMF / H2, (g + 1) * NMF / H2);
+#pragma unroll
+            for (int f = g * NF / H2; f < (g + 1) * NF / H2; ++f) read_frag(kt, 1, 1, f);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        if (H2 == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(kt, 1, 1);
+            mfma(0);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        // substeps 1..NSUB-2 (deeper k-tiles only)
+#pragma unroll
+        for (int sub = 1; sub + 1 < NSUB; ++sub) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(kt, sub + 1, (sub + 1) & 1);
+            mfma(sub & 1);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // tile kt+1 complete in every wave's view; nobody reads stage kt % NS any more
         wait_vmcnt<(G::NS - 2) * NDMA>();
         wait_lgkm0();
         lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        // substep 1: refill this stage with tile kt+NS, first fragments of tile kt+1
-        issue_tile(kt + G::NS);
-        read_frags(kt + 1, 0, 0);
-        mfma(1);
+        // last substep: MFMAs || first fragments of tile kt+1 || DMAs of tile kt+NS
 #pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int g = 0; g < H1; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(kt + G::NS, g);
+            mfma_range((NSUB - 1) & 1, g * NMF / H1, (g + 1) * NMF / H1);
+#pragma unroll
+            for (int f = g * NF / H1; f < (g + 1) * NF / H1; ++f) read_frag(kt + 1, 0, 0, f);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
