@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd tokens/s and FFN TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "ffn_gemm_traffic_mixtral_T16384_H4096_E8_k2_F14336.json")
 
 
 def parse():
@@ -42,6 +42,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work for the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device-to-device copy of MIB MiB "
+                         "(the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                         "WRITE_SIZE, both with --calibrate-copy) into profiles/pmc_traffic.json")
     return ap.parse_args()
 
 
@@ -59,9 +65,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, per_launch_units: int):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
-    were taken on the current kernel sources and the same workload."""
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources and the same workload."""
     try:
         with open(PMC_FILE) as fh:
             d = json.load(fh)
@@ -69,10 +75,55 @@ def traffic_for(kernel: str, per_launch_units: int):
         return None
     if d.get("source_hash") != kernel_source_hash():
         return None
-    k = d.get("kernels", {}).get(kernel)
-    if not k or k.get("rows") != per_launch_units:
+    if d.get("workload") != workload:
         return None
-    return k.get("hbm_bytes")
+    k = d.get("kernels", {}).get(kernel)
+    return None if not k else k.get("hbm_bytes")
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int = 256):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the expert GEMMs, scaled by
+    what the same counters read for the calibration copy of known size."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        # mean per dispatch, keyed by (kernel, grid size); the calibration copy
+        # is the copy dispatch with the largest grid
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        acc, copy = {}, (0, None)
+        for r in rows:
+            v, g = float(r["Counter_Value"]), int(r["Grid_Size"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                if g > copy[0]:
+                    copy = (g, v)
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(v)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, copy[1]
+
+    (fetch, c_fetch), (write, c_write) = (per_kernel(fetch_dir, "FETCH_SIZE"),
+                                          per_kernel(write_dir, "WRITE_SIZE"))
+    if c_fetch is None or c_write is None:
+        raise SystemExit("no calibration copy kernel found in the pmc runs")
+    ck = "__amd_rocclr_copyBuffer"
+    kib = copy_mib * 1024.0
+    f_fetch, f_write = c_fetch / kib, c_write / kib
+    out = {"source_hash": kernel_source_hash(), "workload": workload, "calibration_kernel": ck,
+           "calibration_copy_kib": kib, "fetch_factor": f_fetch, "write_factor": f_write,
+           "kernels": {}}
+    lines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |", "|---|---|---|---|"]
+    for k in sorted(fetch):
+        if "ffn_gemm_bf16" not in k:
+            continue
+        name = "ffn_gemm_bf16_up" if k.split(">")[0].endswith(" 1") else "ffn_gemm_bf16_down"
+        hbm = (fetch[k] / f_fetch + write.get(k, 0.0) / f_write) * 1024.0
+        out["kernels"][name] = {"symbol": k, "fetch_kib": fetch[k], "write_kib": write.get(k),
+                                "hbm_bytes": hbm}
+        lines.append(f"| {name} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {hbm:.4g} |")
+    return out, lines
 
 
 def cpu_baseline(spec, inp, target_s: float):
@@ -109,6 +160,16 @@ def cpu_baseline(spec, inp, target_s: float):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        import workloads as W
+        out, lines = summarize_pmc(*args.summarize_pmc, W.CONFIGS[args.config].name,
+                                   args.calibrate_copy or 256)
+        with open(PMC_FILE, "w") as fh:
+            json.dump(out, fh, indent=1)
+        print("\n".join(lines))
+        print(f"fetch factor {out['fetch_factor']:.4f}, write factor {out['write_factor']:.4f} "
+              f"(calibration: {out['calibration_kernel']})")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -153,6 +214,14 @@ def main():
         moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], out,
                         losses, ws, offsets=offsets, events=ev)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -202,7 +271,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": kern, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_for(kern, A)},
+                     "traffic": traffic_for(kern, spec.name)},
         "ffn_tflops": ffn_tflops,
         "ffn_frac_of_bf16_peak": ffn_tflops / PEAK_BF16_TFLOPS,
         "stage_ms": sm,
