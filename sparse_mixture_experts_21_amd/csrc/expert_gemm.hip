@@ -81,7 +81,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 template <int BM>
 struct Cfg {
     static constexpr int BN = 256, BK = MOE_GEMM_BK;  // k-tile depth
-    static constexpr int NS = MOE_GEMM_NS;            // LDS stages (power of 2)
+    static constexpr int NS = MOE_GEMM_NS;            // LDS stages
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
@@ -96,7 +96,10 @@ struct Cfg {
     static constexpr int XI = X_BYTES / 4096;        // 1 KB DMA blocks per wave (rows)
     static constexpr int GM = MOE_GEMM_GM;           // m-tiles per tile group (L2 reuse)
     static_assert(BK == 32 || BK == 64, "k-tile depth");
-    static_assert((NS & (NS - 1)) == 0 && NS >= 2, "stages");
+    static_assert(NS >= 2, "stages");
+    static constexpr int OP = BN * 2 + 16;           // output staging row pitch (bytes)
+    static constexpr int BM_ROWS = BM;
+    static constexpr int LDS_BYTES = (NS * STAGE > BM * OP) ? NS * STAGE : BM * OP;
 };
 
 // Raw buffer resource: accesses at byte offsets >= num_records return zero
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt, int Nt) {
     using G = Cfg<BM>;
-    __shared__ __attribute__((aligned(1024))) char lds[G::NS * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
 
     int mt, nt;
     tile_coords(blockIdx.x, gridDim.x, Mt, Nt, G::GM, mt, nt);
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     // DMA number q (0 <= q < WI + XI) of k-tile t, into stage t % NS.  k-tiles
     // past the end read at out-of-range offsets and fill the stage with zeros.
     auto issue_one = [&](int t, int q) {
-        const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
+        const uint32_t st = lds0 + (uint32_t)((t % G::NS) * G::STAGE);
         const int k0 = t * G::BK;
         if (q < G::WI) {
             dma16(w_rsrc, woff[q] + (uint32_t)t * wstep,
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     // fragment f (f < FN: weights via two transposed reads; else rows) of
     // k-substep kk of k-tile t into register buffer buf
     auto read_frag = [&](int t, int kk, int buf, int f) {
-        const uint32_t st = lds0 + (uint32_t)((t & (G::NS - 1)) * G::STAGE);
+        const uint32_t st = lds0 + (uint32_t)((t % G::NS) * G::STAGE);
         if (f < G::FN) {
             const uint32_t a = st + aoff[f] + (uint32_t)(kk * 16 * 512);
             const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -368,14 +371,21 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
 
-    // ---- epilogue: D[n][m]; lane owns m = l32 and n = 8 g + 4 half + 0..3
+    // ---- epilogue.  D[n][m]: a lane owns m = l32 and n = 8 g + 4 half + 0..3 of
+    // each 32x32 tile.  Bias and activation in fp32, one rounding to bf16, then
+    // the whole output tile is staged in LDS ([m][n], 528-byte pitch: the
+    // 8-byte writes of 16 consecutive rows and the 16-byte reads of one row are
+    // both bank-conflict free) and written out as full contiguous row
+    // segments, so every 128-byte line of the output is written once.
+    wait_lgkm0();
+    lds_barrier();
     const uint16_t* be = bias ? bias + (int64_t)e * N : nullptr;
 #pragma unroll
     for (int i = 0; i < G::FN; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * G::TN + 32 * i + 8 * g + 4 * half;
-            if (n >= N) continue;
+            const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
+            const int n = min(n0 + nl, N - 4);
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if (be) {
                 const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(be + n);
@@ -386,8 +396,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
             }
 #pragma unroll
             for (int j = 0; j < G::FM; ++j) {
-                const int m = m0 + wm * G::TM + 32 * j + l32;
-                if (m >= n_rows) continue;
+                const int ml = wm * G::TM + 32 * j + l32;
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -397,9 +406,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
                 u32x2_t o;
                 o[0] = pack_bf16x2(v[0], v[1]);
                 o[1] = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<u32x2_t*>(C + (int64_t)(row_begin + m) * N + n) = o;
+                *reinterpret_cast<u32x2_t*>(lds + ml * G::OP + nl * 2) = o;
             }
         }
+    }
+    lds_barrier();
+    const int rows = min(G::BM_ROWS, n_rows - m0);
+    const int chunks = min(G::BN, N - n0) / 8;            // 16-byte chunks per row (N % 8 == 0)
+    uint16_t* cbase = C + (int64_t)(row_begin + m0) * N + n0;
+    for (int idx = tid; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
+        const int r = idx / (G::BN / 8), c = idx % (G::BN / 8);
+        if (r < rows && c < chunks)
+            *reinterpret_cast<u32x4_t*>(cbase + (int64_t)r * N + c * 8) =
+                *reinterpret_cast<const u32x4_t*>(lds + r * G::OP + c * 16);
     }
 }
 
