@@ -75,9 +75,6 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 4
 #endif
-#ifndef MOE_GEMM_GM
-#define MOE_GEMM_GM 8
-#endif
 template <int BM>
 struct Cfg {
     static constexpr int BN = 256, BK = MOE_GEMM_BK;  // k-tile depth
@@ -94,7 +91,6 @@ struct Cfg {
     static constexpr int STAGE = W_BYTES + X_BYTES;
     static constexpr int WI = W_BYTES / 4096;        // 1 KB DMA blocks per wave (weights)
     static constexpr int XI = X_BYTES / 4096;        // 1 KB DMA blocks per wave (rows)
-    static constexpr int GM = MOE_GEMM_GM;           // m-tiles per tile group (L2 reuse)
     static_assert(BK == 32 || BK == 64, "k-tile depth");
     static_assert(NS >= 2, "stages");
     static constexpr int OP = BN * 2 + 16;           // output staging row pitch (bytes)
@@ -138,21 +134,30 @@ typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
-// Workgroup -> (row tile, column tile).  The hardware deals workgroups to the
-// 8 XCDs round-robin; remap so that each XCD walks a contiguous range of the
-// logical order, and order that range in groups of GM row tiles x all column
-// tiles so the ~32 tiles an XCD runs at once share X and W slices in its L2.
-__device__ __forceinline__ void tile_coords(int b, int nblk, int Mt, int Nt, int GM, int& mt,
-                                            int& nt) {
-    const int x = b & 7, j = b >> 3;
-    const int q = nblk >> 3, r = nblk & 7;
-    const int lid = x * q + min(x, r) + j;
-    const int per_group = GM * Nt;
-    const int g = lid / per_group, w = lid % per_group;
-    const int m_base = g * GM;
-    const int gm = min(GM, Mt - m_base);
-    mt = m_base + w % gm;
-    nt = w / gm;
+// Workgroup -> (row tile, column tile).  The grid is a sequence of
+// super-blocks of 256 tiles (SBM row tiles x SBN column tiles, one tile per
+// CU), walked row-major.  The hardware deals workgroups to the 8 XCDs
+// round-robin, so position p of a super-block runs on XCD p % 8; each XCD
+// gets an 8 x 4 sub-block of it (rotating with the super-block index).  Inside an XCD the ~32 resident tiles share
+// their row and weight slabs in its L2; across XCDs the whole chip works on
+// one super-block at a time, so slabs another XCD already pulled are served
+// from the memory-side cache instead of HBM.  Positions past the last real
+// tile return at once.
+__device__ __forceinline__ void tile_coords(int b, int SBN, int nsbn, int nsbm, int& mt, int& nt) {
+    const int sb = b >> 8, p = b & 255;
+    const int x = p & 7, j = p >> 3;                     // XCD, slot on the XCD
+#ifdef MOE_GEMM_SB_COLMAJOR
+    const int sbm = sb % nsbm, sbn = sb / nsbm;
+#else
+    const int sbm = sb / nsbn, sbn = sb % nsbn;
+    (void)nsbm;
+#endif
+    // XCD x takes sub-block (x + sb) % 8: the rotation spreads the tiles of a
+    // partial (ragged) super-block over all XCDs instead of a fixed few
+    const int s8 = (x + sb) & 7;
+    const int xm = s8 % (256 / SBN / 8), xn = s8 / (256 / SBN / 8);  // sub-block
+    mt = sbm * (256 / SBN) + xm * 8 + (j & 7);
+    nt = sbn * SBN + xn * 4 + (j >> 3);
 }
 
 // LDS layouts (per stage):
@@ -169,13 +174,15 @@ template <int BM, int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt, int Nt) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt, int Nt,
+    int SBN) {
     using G = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
 
     int mt, nt;
-    tile_coords(blockIdx.x, gridDim.x, Mt, Nt, G::GM, mt, nt);
+    tile_coords(blockIdx.x, SBN, (Nt + SBN - 1) / SBN, (Mt + 256 / SBN - 1) / (256 / SBN), mt, nt);
     int e, m0, row_begin, n_rows;
+    if (nt >= Nt || mt >= Mt) return;
     if (!find_tile<BM>(offsets, E, mt, e, m0, row_begin, n_rows)) return;
     const int n0 = nt * G::BN;
 
@@ -264,9 +271,12 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
             fb[buf][j] = *(const lds_bf16x8_t*)(uintptr_t)b;
         }
     };
+    // Fragments in the order the next substep's MFMAs consume them (row-major
+    // over the accumulator tiles): A0, B0..B(FM-1), A1..A(FN-1).
+    auto frag_id = [](int o) { return o == 0 ? 0 : (o <= G::FM ? G::FN + o - 1 : o - G::FM); };
     auto read_frags = [&](int t, int kk, int buf) {
 #pragma unroll
-        for (int f = 0; f < G::FN + G::FM; ++f) read_frag(t, kk, buf, f);
+        for (int o = 0; o < G::FN + G::FM; ++o) read_frag(t, kk, buf, frag_id(o));
     };
 
     f32x16_t acc[G::FN][G::FM];
@@ -299,6 +309,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     constexpr int H1 = (NDMA + 1) / 2, H2 = NDMA - H1;
     constexpr int NSUB = G::BK / 16;         // 16-deep MFMA k-substeps per k-tile
     constexpr int NF = G::FN + G::FM;        // fragments per substep
+    // the fragment reads of a substep go into its first half of MFMA groups,
+    // so they land well before the next substep's first MFMA needs them
+    constexpr int RG2 = H2 > 1 ? H2 / 2 : 1, RG1 = H1 > 1 ? H1 / 2 : 1;
     const int nk = (K + G::BK - 1) / G::BK;
 #pragma unroll
     for (int t = 0; t + 1 < G::NS; ++t)
@@ -318,12 +331,15 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
             __builtin_amdgcn_sched_barrier(0);
             issue_one(kt + G::NS - 1, H1 + g);
             mfma_range(0, g * NMF / H2, (g + 1) * NMF / H2);
+            if (g < RG2) {
 #pragma unroll
-            for (int f = g * NF / H2; f < (g + 1) * NF / H2; ++f) read_frag(kt, 1, 1, f);
+                for (int o = g * NF / RG2; o < (g + 1) * NF / RG2; ++o)
+                    read_frag(kt, 1, 1, frag_id(o));
+            }
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         }
         if (H2 == 0) {
@@ -359,12 +375,15 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
             __builtin_amdgcn_sched_barrier(0);
             issue_one(kt + G::NS, g);
             mfma_range((NSUB - 1) & 1, g * NMF / H1, (g + 1) * NMF / H1);
+            if (g < RG1) {
 #pragma unroll
-            for (int f = g * NF / H1; f < (g + 1) * NF / H1; ++f) read_frag(kt + 1, 0, 0, f);
+                for (int o = g * NF / RG1; o < (g + 1) * NF / RG1; ++o)
+                    read_frag(kt + 1, 0, 0, frag_id(o));
+            }
 #pragma unroll
             for (int q = 0; q < NMF; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         }
     }
@@ -509,7 +528,14 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         const int bm = pick_bm(p);
         const int Mt = (int)((rows + bm - 1) / bm + p.E);
         const int Nt = (N + 255) / 256;
-        const dim3 grid((unsigned)((int64_t)Mt * Nt)), block(256);
+        // super-block width in column tiles: the widest of 16/8/4 that divides Nt
+#ifdef MOE_GEMM_SBN
+        const int SBN = MOE_GEMM_SBN;
+#else
+        const int SBN = (Nt % 16 == 0) ? 16 : (Nt % 8 == 0) ? 8 : 4;
+#endif
+        const int64_t nsb = (int64_t)((Mt + 256 / SBN - 1) / (256 / SBN)) * ((Nt + SBN - 1) / SBN);
+        const dim3 grid((unsigned)(nsb * 256)), block(256);
         auto* x = static_cast<const uint16_t*>(X);
         auto* w = static_cast<const uint16_t*>(W);
         auto* b = static_cast<const uint16_t*>(bias);
@@ -518,11 +544,11 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
         if (bm == 256)
-            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
+            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
         else if (bm == 128)
-            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
+            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
         else
-            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt);
+            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
         const int Nt = (N + 63) / 64;
