@@ -4,13 +4,17 @@
 // Parallelism: capacity factor and dropping tokens over capacity).
 //
 // Per expert the first `cap` (token, slot) pairs in ascending token order are
-// kept.  The pairs are cut into chunks of kChunkTok tokens:
-//   1. chunk_hist   per-chunk expert histogram (LDS integer atomics; the
-//                   result is order independent, hence deterministic);
-//   2. chunk_scan   per expert, exclusive scan over chunks -> the number of
-//                   earlier pairs routed to e before each chunk; kept counts
-//                   min(count, cap) and their exclusive scan -> offsets;
-//   3. chunk_rank   one wave walks its chunk 64 pairs at a time in token
+// kept.  The pairs are cut into chunks of kChunkTok tokens (one router block):
+//   1. chunk_hist   per-chunk expert histogram, column-major [E][nchunk] (LDS
+//                   integer atomics; order independent, hence deterministic).
+//                   The fused forward skips it: the router already wrote
+//                   exactly this table as its per-block expert counts;
+//   2. scan_columns per expert (one workgroup each), exclusive scan over
+//                   chunks -> the number of earlier pairs routed to e before
+//                   each chunk, and the expert's total;
+//   3. chunk_rank   kept counts min(total, cap) and their exclusive scan ->
+//                   offsets (every workgroup forms them from the E totals);
+//                   then one wave walks its chunk 64 pairs at a time in token
 //                   order; lanes routed to the same expert find each other
 //                   with 8 ballots over the expert id bits, and the rank is
 //                   the running per-expert count plus the number of matching
@@ -18,68 +22,135 @@
 //   4. gather_rows  xp[r] = x[row_token[r]] with 16-byte copies (skipped when
 //                   the first expert GEMM reads x through row_token itself).
 #include "moe_internal.h"
+#include "route_finalize.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void chunk_hist(const int32_t* __restrict__ topk_idx,
-                                                  int64_t T, int E, int k,
-                                                  int32_t* __restrict__ hist) {
+__global__ __launch_bounds__(64) void chunk_hist(const int32_t* __restrict__ topk_idx,
+                                                 int64_t T, int E, int k,
+                                                 int32_t* __restrict__ hist) {
     __shared__ int32_t h[kMaxE];
     const int tid = threadIdx.x;
-    const int64_t c = blockIdx.x;
-    for (int e = tid; e < E; e += 256) h[e] = 0;
+    const int64_t c = blockIdx.x, nchunk = gridDim.x;
+    for (int e = tid; e < E; e += 64) h[e] = 0;
     __syncthreads();
     const int64_t j0 = c * kChunkTok * k;
     const int64_t j1 = min((c + 1) * kChunkTok, T) * k;
-    for (int64_t j = j0 + tid; j < j1; j += 256) {
+    for (int64_t j = j0 + tid; j < j1; j += 64) {
         const int e = topk_idx[j];
         if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // invalid ids are dropped
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 256) hist[c * E + e] = h[e];
+    for (int e = tid; e < E; e += 64) hist[e * nchunk + c] = h[e];
 }
 
-__global__ __launch_bounds__(256) void chunk_scan(const int32_t* __restrict__ hist,
-                                                  int64_t nchunk, int E, int32_t cap,
-                                                  int32_t* __restrict__ base,
-                                                  int32_t* __restrict__ offsets) {
-    __shared__ int32_t kept[kMaxE];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 256) {
-        int32_t run = 0;
-        for (int64_t c = 0; c < nchunk; ++c) {
-            base[c * E + e] = run;
-            run += hist[c * E + e];
-        }
-        kept[e] = min(run, cap);
+// Workgroup e < E scans expert column e: thread t takes kColPer consecutive
+// chunks of each round (one round of loads), the thread totals get an
+// exclusive scan (shuffles within each wave, the 4 wave totals through LDS),
+// and each thread writes its chunks' running prefix; the column total goes to
+// col_tot[e].  With FIN the workgroups E .. 2E sum the router's per-block
+// partials (one column each), which saves the fused forward two launches.
+template <bool FIN>
+__global__ __launch_bounds__(kColThreads) void scan_columns(const int32_t* __restrict__ hist,
+                                                           int64_t nchunk, int E,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ col_tot,
+                                                           FinArgs fin) {
+    __shared__ int32_t wtot[kColThreads / 64];
+    const int col = blockIdx.x;
+    if (FIN && col >= E) {
+        fin_column_block(fin, E, col - E);
+        return;
     }
-    __syncthreads();
-    if (tid == 0) {
-        int32_t acc = 0;
-        for (int e = 0; e < E; ++e) {
-            offsets[e] = acc;
-            acc += kept[e];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t* src = hist + (int64_t)col * nchunk;
+    int32_t* dst = base + (int64_t)col * nchunk;
+    int32_t carry = 0;
+    for (int64_t s0 = 0; s0 < nchunk; s0 += kColThreads * kColPer) {
+        const int64_t c0 = s0 + (int64_t)tid * kColPer;
+        int32_t v[kColPer];
+#pragma unroll
+        for (int i = 0; i < kColPer; ++i)          // clamped, masked: no per-load branch
+            v[i] = src[c0 + i < nchunk ? c0 + i : nchunk - 1];
+        int32_t tot = 0;
+#pragma unroll
+        for (int i = 0; i < kColPer; ++i) {
+            if (c0 + i >= nchunk) v[i] = 0;
+            tot += v[i];
         }
-        offsets[E] = acc;
+        int32_t incl = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        if (lane == 63) wtot[wave] = incl;
+        __syncthreads();
+        int32_t before = 0, round = 0;
+#pragma unroll
+        for (int w = 0; w < kColThreads / 64; ++w) {
+            if (w < wave) before += wtot[w];
+            round += wtot[w];
+        }
+        __syncthreads();                           // wtot is rewritten next round
+        int32_t run = carry + before + incl - tot;
+#pragma unroll
+        for (int i = 0; i < kColPer; ++i) {
+            if (c0 + i < nchunk) dst[c0 + i] = run;
+            run += v[i];
+        }
+        carry += round;
     }
+    if (tid == 0) col_tot[col] = carry;
 }
 
+// Every workgroup derives offsets[] from the column totals itself (kept count
+// min(total, cap), exclusive scan over the experts); workgroup 0 publishes
+// them and, with FIN, the router's expert counts and losses.
+template <bool FIN>
 __global__ __launch_bounds__(64) void chunk_rank(const int32_t* __restrict__ topk_idx,
                                                  const int32_t* __restrict__ base,
-                                                 const int32_t* __restrict__ offsets, int64_t T,
+                                                 const int32_t* __restrict__ col_tot, int64_t T,
                                                  int E, int k, int32_t cap,
+                                                 int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ pos,
-                                                 int32_t* __restrict__ row_token) {
+                                                 int32_t* __restrict__ row_token, FinArgs fin) {
     __shared__ int32_t run[kMaxE];
-    __shared__ int32_t off[kMaxE];
+    __shared__ int32_t off[kMaxE + 1];
     const int lane = threadIdx.x;
-    const int64_t c = blockIdx.x;
-    for (int e = lane; e < E; e += 64) {
-        run[e] = base[c * E + e];
-        off[e] = offsets[e];
+    const int64_t c = blockIdx.x, nchunk = gridDim.x;
+    {
+        // lane l owns experts 4l .. 4l + 3 (E <= 256)
+        int32_t kv[4], tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            kv[i] = min(col_tot[e < E ? e : E - 1], cap);   // unconditional load, masked
+            if (e >= E) kv[i] = 0;
+            tot += kv[i];
+        }
+        int32_t incl = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        int32_t o = incl - tot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) off[e] = o;
+            o += kv[i];
+        }
+        if (lane == 63) off[E] = incl;
     }
+    for (int e = lane; e < E; e += 64) run[e] = base[e * nchunk + c];
     __syncthreads();
+    if (c == 0) {
+        for (int e = lane; e <= E; e += 64) offsets[e] = off[e];
+        if (FIN && lane == 0) fin_losses(fin, E);
+    }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int64_t j0 = c * kChunkTok * k;
     const int64_t j1 = min((c + 1) * kChunkTok, T) * k;
@@ -137,17 +208,35 @@ __global__ __launch_bounds__(256) void gather_rows(const u32x4_t* __restrict__ x
 
 hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, int64_t cap,
                           const void* x, const int32_t* topk_idx, int32_t* offsets,
-                          int32_t* pos, int32_t* row_token, void* xp, hipStream_t s) {
+                          int32_t* pos, int32_t* row_token, void* xp, int32_t* fin_counts,
+                          float* fin_losses, hipStream_t s) {
     const int64_t T = p.T;
     const int E = p.E, k = p.k;
     const int64_t nchunk = L.nchunk;
     int32_t* hist = reinterpret_cast<int32_t*>(ws + L.chunk_hist);
     int32_t* base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+    int32_t* tot = reinterpret_cast<int32_t*>(ws + L.col_tot);
     const int32_t cap32 = (int32_t)std::min<int64_t>(cap, (int64_t)0x7fffffff);
-    chunk_hist<<<dim3((unsigned)nchunk), dim3(256), 0, s>>>(topk_idx, T, E, k, hist);
-    chunk_scan<<<dim3(1), dim3(256), 0, s>>>(hist, nchunk, E, cap32, base, offsets);
-    chunk_rank<<<dim3((unsigned)nchunk), dim3(64), 0, s>>>(topk_idx, base, offsets, T, E, k,
-                                                          cap32, pos, row_token);
+    if (fin_counts && fin_losses) {
+        // fused forward: the router's per-block expert counts are the chunk
+        // histogram, and its partials are reduced alongside the scan
+        const FinArgs f{reinterpret_cast<const float*>(ws + L.blk_psum),
+                        reinterpret_cast<const float*>(ws + L.blk_lse2),
+                        reinterpret_cast<const int32_t*>(ws + L.blk_cnt), L.nblk_route, T, k,
+                        reinterpret_cast<double*>(ws + L.fin_sum),
+                        reinterpret_cast<long long*>(ws + L.fin_cnt), fin_counts, fin_losses};
+        hist = reinterpret_cast<int32_t*>(ws + L.blk_cnt);
+        scan_columns<true><<<dim3(2 * E + 1), dim3(kColThreads), 0, s>>>(hist, nchunk, E, base,
+                                                                         tot, f);
+        chunk_rank<true><<<dim3((unsigned)nchunk), dim3(64), 0, s>>>(
+            topk_idx, base, tot, T, E, k, cap32, offsets, pos, row_token, f);
+    } else {
+        chunk_hist<<<dim3((unsigned)nchunk), dim3(64), 0, s>>>(topk_idx, T, E, k, hist);
+        scan_columns<false><<<dim3(E), dim3(kColThreads), 0, s>>>(hist, nchunk, E, base, tot,
+                                                                  FinArgs{});
+        chunk_rank<false><<<dim3((unsigned)nchunk), dim3(64), 0, s>>>(
+            topk_idx, base, tot, T, E, k, cap32, offsets, pos, row_token, FinArgs{});
+    }
     if (xp) {
         const int64_t row_bytes = (int64_t)p.H * (p.dtype == MOE_DTYPE_BF16 ? 2 : 4);
         const int64_t vec = row_bytes / 16;

@@ -24,6 +24,7 @@
 // fragment reads for the next k-substep are interleaved with the MFMAs of
 // the current one, and one barrier per k-tile orders DMA and reads.
 #include "moe_internal.h"
+#include "lds_dma.h"
 
 namespace moe {
 namespace {
@@ -97,37 +98,6 @@ struct Cfg {
     static constexpr int BM_ROWS = BM;
     static constexpr int LDS_BYTES = (NS * STAGE > BM * OP) ? NS * STAGE : BM * OP;
 };
-
-// Raw buffer resource: accesses at byte offsets >= num_records return zero
-// without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-constexpr uint32_t kOob = 0x80000000u;   // an offset beyond every resource's range
-
-// 16 bytes per lane from global memory straight into LDS (M0 + 16 * lane);
-// no VGPR is written, so nothing is left in flight in registers.  Completion
-// is tracked with vmcnt by the caller.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory");
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding; lgkmcnt and expcnt left unconstrained).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));

@@ -30,11 +30,12 @@ WsLayout ws_layout(const moe_problem_t& p) {
     L.blk_psum = take(nb * E * 4);
     L.blk_lse2 = take(nb * 4);
     L.blk_cnt = take(nb * E * 4);
-    L.fin = take((E + 1) * 8);
+    L.fin_sum = take((E + 1) * 8);
+    L.fin_cnt = take(E * 8);
     L.route_bytes = off;
     L.chunk_hist = take(nc * E * 4);
     L.chunk_base = take(nc * E * 4);
-    L.misc = take(256);
+    L.col_tot = take(E * 4);
     L.permute_bytes = off;
     L.ffn_bytes = 0;
     L.logits = 0;                 // moe_forward never stores logits in the workspace
@@ -128,7 +129,7 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* Wg, co
     const WsLayout L = ws_layout(*p);
     if (ws_bytes < L.route_bytes) return MOE_ERR_WORKSPACE;
     hipError_t e = launch_route(*p, L, static_cast<char*>(ws), x, Wg, bg, logits, logits_in,
-                                topk_idx, topk_w, counts, losses, stream);
+                                topk_idx, topk_w, counts, losses, true, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -145,7 +146,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* x, const int32_t* t
     const WsLayout L = ws_layout(*p);
     if (ws_bytes < L.permute_bytes) return MOE_ERR_WORKSPACE;
     hipError_t e = launch_permute(*p, L, static_cast<char*>(ws), capacity_of(*p), x, topk_idx,
-                                  offsets, pos, row_token, xp, stream);
+                                  offsets, pos, row_token, xp, nullptr, nullptr, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -211,10 +212,12 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
     };
     hipError_t e = ev(MOE_EV_ROUTE);
     if (e == hipSuccess)
-        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, stream);
+        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, false,
+                         stream);
     if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
     if (e == hipSuccess)
-        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, stream);
+        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt, losses,
+                           stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
     if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);

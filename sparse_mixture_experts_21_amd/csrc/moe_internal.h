@@ -39,14 +39,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // regions are 256-byte aligned.  Regions a call does not use are still laid
 // out so that one layout serves every entry point.
 struct WsLayout {
-    size_t wgt;          // gate weights transposed to [E][H] (bf16 router)
-    size_t blk_psum;     // [nblk_route][E] fp32: per-block sums of softmax probs
+    size_t wgt;          // gate weights transposed to [E][H] (bf16 router, E > 16)
+    size_t blk_psum;     // [E][nblk_route] fp32: per-block sums of softmax probs
     size_t blk_lse2;     // [nblk_route]    fp32: per-block sums of lse^2
-    size_t blk_cnt;      // [nblk_route][E] int32: per-block expert histograms
-    size_t fin;          // finalize scratch: [E] double + ticket
-    size_t chunk_hist;   // [nchunk][E] int32
-    size_t chunk_base;   // [nchunk][E] int32
-    size_t misc;         // small scalars (kept rows total, ...)
+    size_t blk_cnt;      // [E][nblk_route] int32: per-block expert histograms
+    size_t fin_sum;      // [E + 1] fp64: column sums of the router partials
+    size_t fin_cnt;      // [E] int64: expert counts from the router partials
+    size_t chunk_hist;   // [E][nchunk] int32 expert histogram per chunk
+    size_t chunk_base;   // [E][nchunk] int32 pairs routed to e before the chunk
+    size_t col_tot;      // [E] int32: pairs routed to each expert
     // moe_forward intermediates, used when the caller passes NULL
     size_t logits, topk_idx, topk_w, counts, offsets, pos, row_token, xp, h, y;
     size_t route_bytes, permute_bytes, ffn_bytes, total;
@@ -54,19 +55,26 @@ struct WsLayout {
 };
 
 constexpr int kRouteTok = 16;      // tokens per router workgroup
-constexpr int kChunkTok = 128;     // tokens per dispatch chunk
+constexpr int kChunkTok = 16;      // tokens per dispatch chunk: one router block, so the
+                                   // router's per-block histograms are the chunk histograms
+static_assert(kChunkTok == kRouteTok, "dispatch chunks are router blocks");
 
 WsLayout ws_layout(const moe_problem_t& p);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.
+// finalize = false leaves the per-block partials in the workspace for the next
+// launch_permute (given fin_counts / fin_losses) to reduce.
 hipError_t launch_route(const moe_problem_t& p, const WsLayout& L, char* ws, const void* x,
                         const void* Wg, const void* bg, float* logits, bool logits_in,
                         int32_t* topk_idx, float* topk_w, int32_t* counts, float* losses,
-                        hipStream_t s);
+                        bool finalize, hipStream_t s);
+// fin_counts / fin_losses (both or neither): also reduce the router partials
+// that a launch_route with finalize = false left in the workspace.
 hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, int64_t cap,
                           const void* x, const int32_t* topk_idx, int32_t* offsets,
-                          int32_t* pos, int32_t* row_token, void* xp, hipStream_t s);
+                          int32_t* pos, int32_t* row_token, void* xp, int32_t* fin_counts,
+                          float* fin_losses, hipStream_t s);
 // rowmap (nullable): when set, row r of the first GEMM reads x[rowmap[r]]
 // instead of xp[r] (the gather fused into the operand load).
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
