@@ -9,42 +9,84 @@
 namespace moe {
 namespace {
 
-// One thread = one 16-byte vector of one token row (8 bf16 or 4 fp32).
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+// y is read once and out written once: nontemporal, so neither allocates in
+// (nor first has to write back dirty lines of) the last-level cache.
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+    return MOE_COMBINE_NT ? __builtin_nontemporal_load(p) : *p;
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, V v) {
+    if (MOE_COMBINE_NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// One workgroup = one token row; a thread owns kCombVec 16-byte vectors
+// (8 bf16 or 4 fp32 each) per pass.  The token's k (row, weight) pairs are
+// workgroup-uniform; every kept slot's vectors are loaded before the sum,
+// which runs in fp32 in slot order and is rounded once.
+constexpr int kCombThreads = 256;
+constexpr int kCombVec = 2;
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_rows(const u32x4_t* __restrict__ y,
-                                                    const int32_t* __restrict__ pos,
-                                                    const float* __restrict__ topk_w,
-                                                    int64_t T, int k, int64_t vec,
-                                                    u32x4_t* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * vec) return;
-    const int64_t t = i / vec, v = i % vec;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < k; ++s) {
-        const int32_t r = pos[t * k + s];
-        if (r < 0) continue;
-        const float w = topk_w[t * k + s];
-        const u32x4_t d = y[(int64_t)r * vec + v];
-        if (BF16) {
+__global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __restrict__ y,
+                                                             const int32_t* __restrict__ pos,
+                                                             const float* __restrict__ topk_w,
+                                                             int k, int64_t vec,
+                                                             u32x4_t* __restrict__ out) {
+    const int64_t t = blockIdx.x;
+    int32_t row[kMaxK];
+    float w[kMaxK];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(w, bf16_lo(d[q]), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(w, bf16_hi(d[q]), acc[2 * q + 1]);
+    for (int s = 0; s < kMaxK; ++s) {
+        row[s] = s < k ? pos[t * k + s] : -1;
+        w[s] = s < k ? topk_w[t * k + s] : 0.f;
+    }
+    for (int64_t v0 = threadIdx.x; v0 < vec; v0 += kCombThreads * kCombVec) {
+        u32x4_t d[kMaxK][kCombVec];
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            if (row[s] < 0) continue;                  // uniform: no divergence
+#pragma unroll
+            for (int u = 0; u < kCombVec; ++u) {
+                const int64_t v = v0 + (int64_t)u * kCombThreads;
+                if (v < vec) d[s][u] = ld_stream(&y[(int64_t)row[s] * vec + v]);
             }
-        } else {
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, __uint_as_float(d[q]), acc[q]);
+        for (int u = 0; u < kCombVec; ++u) {
+            const int64_t v = v0 + (int64_t)u * kCombThreads;
+            if (v >= vec) continue;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kMaxK; ++s) {
+                if (row[s] < 0) continue;
+                if (BF16) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = fmaf(w[s], bf16_lo(d[s][u][q]), acc[2 * q]);
+                        acc[2 * q + 1] = fmaf(w[s], bf16_hi(d[s][u][q]), acc[2 * q + 1]);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[q] = fmaf(w[s], __uint_as_float(d[s][u][q]), acc[q]);
+                }
+            }
+            u32x4_t o;
+            if (BF16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+            }
+            st_stream(&out[t * vec + v], o);
         }
     }
-    u32x4_t o;
-    if (BF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
-    }
-    out[i] = o;
 }
 
 }  // namespace
@@ -53,16 +95,13 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* 
                           const float* topk_w, void* out, hipStream_t s) {
     const bool bf16 = p.dtype == MOE_DTYPE_BF16;
     const int64_t vec = (int64_t)p.H * (bf16 ? 2 : 4) / 16;
-    const int64_t n = p.T * vec;
-    const unsigned nb = (unsigned)((n + 255) / 256);
+    const unsigned nb = (unsigned)p.T;
     if (bf16)
-        combine_rows<true><<<dim3(nb), dim3(256), 0, s>>>(static_cast<const u32x4_t*>(y), pos,
-                                                          topk_w, p.T, p.k, vec,
-                                                          static_cast<u32x4_t*>(out));
+        combine_rows<true><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
+            static_cast<const u32x4_t*>(y), pos, topk_w, p.k, vec, static_cast<u32x4_t*>(out));
     else
-        combine_rows<false><<<dim3(nb), dim3(256), 0, s>>>(static_cast<const u32x4_t*>(y), pos,
-                                                           topk_w, p.T, p.k, vec,
-                                                           static_cast<u32x4_t*>(out));
+        combine_rows<false><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
+            static_cast<const u32x4_t*>(y), pos, topk_w, p.k, vec, static_cast<u32x4_t*>(out));
     return hipGetLastError();
 }
 
