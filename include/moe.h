@@ -136,7 +136,11 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* x, const int32_t* t
  * rows of each expert, as one grouped GEMM pair over unequal groups:
  *   h[r] = GELU(xp[r] . W1[e] + b1[e])   with exact GELU 0.5 a (1 + erf(a/sqrt2)),
  *   y[r] = h[r] . W2[e] + b2[e]          for offsets[e] <= r < offsets[e+1].
- * h[T*k][F] and y[T*k][H] are written for rows < offsets[E] only. */
+ * h[T*k][F] and y[T*k][H] are written for rows < offsets[E] only.
+ * ws is optional (may be NULL): with a 16-byte aligned workspace of at least
+ * moe_workspace_bytes(p) bytes, the ragged last round of GEMM tiles is split
+ * along K for load balance (fp32 partials summed in a fixed order, so results
+ * stay reproducible); without it every tile is computed whole. */
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_t* offsets,
                             const void* W1, const void* b1, const void* W2, const void* b2,
                             void* h, void* y, void* ws, size_t ws_bytes, hipStream_t stream);

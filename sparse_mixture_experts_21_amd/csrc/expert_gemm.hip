@@ -23,6 +23,11 @@
 // fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
 // fragment reads for the next k-substep are interleaved with the MFMAs of
 // the current one, and one barrier per k-tile orders DMA and reads.
+//
+// Load balance: when the real tiles leave a ragged last round of at most half
+// the CUs, those tiles are cut along K into slices that fill one whole round
+// and write fp32 partials; ffn_gemm_fixup sums them in slice order and applies
+// the epilogue (bias, activation, bf16).
 #include "moe_internal.h"
 #include "lds_dma.h"
 
@@ -49,24 +54,49 @@ __device__ __forceinline__ float gelu_erf(float a) {
 }
 
 // Locate the expert and row tile of row-tile index mt.  Returns false when mt
-// is beyond the last real tile.
+// is beyond the last real tile.  The whole wave walks 64 experts at a time
+// (tile counts, a shuffle scan, a ballot), so the cost grows with E / 64.
 template <int BM>
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt,
                                           int& e_out, int& m0, int& row_begin, int& n_rows) {
+    const int lane = threadIdx.x & 63;
     int base = 0;
-    for (int e = 0; e < E; ++e) {
-        const int b = offsets[e], n = offsets[e + 1] - b;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int b = e < E ? offsets[e] : 0;
+        const int n = e < E ? offsets[e + 1] - b : 0;
         const int tiles = (n + BM - 1) / BM;
-        if (mt < base + tiles) {
-            e_out = e;
-            m0 = (mt - base) * BM;
-            row_begin = b;
-            n_rows = n;
+        int incl = tiles;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        const int excl = incl - tiles;
+        const uint64_t hit = __ballot(e < E && mt >= base + excl && mt < base + incl);
+        if (hit) {
+            // wave-uniform results, pinned to scalar registers
+            const int src = __ffsll((unsigned long long)hit) - 1;
+            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src));
+            m0 = __builtin_amdgcn_readfirstlane((mt - base - __shfl(excl, src)) * BM);
+            row_begin = __builtin_amdgcn_readfirstlane(__shfl(b, src));
+            n_rows = __builtin_amdgcn_readfirstlane(__shfl(n, src));
             return true;
         }
-        base += tiles;
+        base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
     }
     return false;
+}
+
+// Real row tiles over all experts (every lane gets the same value).
+template <int BM>
+__device__ __forceinline__ int real_row_tiles(const int32_t* __restrict__ offsets, int E) {
+    const int lane = threadIdx.x & 63;
+    int t = 0;
+    for (int e = lane; e < E; e += 64) t += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+    return t;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
@@ -97,6 +127,7 @@ struct Cfg {
     static constexpr int OP = BN * 2 + 16;           // output staging row pitch (bytes)
     static constexpr int BM_ROWS = BM;
     static constexpr int LDS_BYTES = (NS * STAGE > BM * OP) ? NS * STAGE : BM * OP;
+    static constexpr int UNIT = BM * BN;             // floats of one fp32 partial tile
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -104,31 +135,87 @@ typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
-// Workgroup -> (row tile, column tile).  The grid is a sequence of
-// super-blocks of 256 tiles (SBM row tiles x SBN column tiles, one tile per
-// CU), walked row-major.  The hardware deals workgroups to the 8 XCDs
-// round-robin, so position p of a super-block runs on XCD p % 8; each XCD
-// gets an 8 x 4 sub-block of it (rotating with the super-block index).  Inside an XCD the ~32 resident tiles share
-// their row and weight slabs in its L2; across XCDs the whole chip works on
-// one super-block at a time, so slabs another XCD already pulled are served
-// from the memory-side cache instead of HBM.  Positions past the last real
-// tile return at once.
-__device__ __forceinline__ void tile_coords(int b, int SBN, int nsbn, int nsbm, int& mt, int& nt) {
-    const int sb = b >> 8, p = b & 255;
-    const int x = p & 7, j = p >> 3;                     // XCD, slot on the XCD
-#ifdef MOE_GEMM_SB_COLMAJOR
-    const int sbm = sb % nsbm, sbn = sb / nsbm;
-#else
-    const int sbm = sb / nsbn, sbn = sb % nsbn;
-    (void)nsbm;
-#endif
-    // XCD x takes sub-block (x + sb) % 8: the rotation spreads the tiles of a
-    // partial (ragged) super-block over all XCDs instead of a fixed few
-    const int s8 = (x + sb) & 7;
-    const int xm = s8 % (256 / SBN / 8), xn = s8 / (256 / SBN / 8);  // sub-block
-    mt = sbm * (256 / SBN) + xm * 8 + (j & 7);
-    nt = sbn * SBN + xn * 4 + (j >> 3);
+// Tile order.  Real tiles get the dense positions 0 .. R-1 (R = real row tiles
+// x Nt; the real row-tile count is computed on the device from `offsets`).
+// Full super-block rows come first: super-blocks of 256 tiles (SBM = 256/SBN
+// row tiles x SBN column tiles, one tile per CU), walked row-major.  The
+// hardware deals workgroups to the 8 XCDs round-robin, so position p runs on
+// XCD p % 8; in each super-block every XCD gets an 8 x 4 sub-block (rotating
+// with the super-block index), so the ~32 tiles resident on one XCD share
+// their row and weight slabs in its L2, and slabs another XCD already pulled
+// come from the memory-side cache.  The remaining (< SBM) row tiles follow,
+// XCD x taking the column tiles nt = x (mod 8) when Nt % 8 == 0.
+__device__ __forceinline__ void dense_coords(int p, int real_mt, int Nt, int SBN, int& mt,
+                                             int& nt) {
+    const int SBM = 256 / SBN;
+    if (Nt % SBN != 0) {                                  // no super-blocks (narrow N)
+        mt = p / Nt;
+        nt = p % Nt;
+        return;
+    }
+    const int F = real_mt / SBM;                          // full super-block rows
+    const int nfull = F * SBM * Nt;
+    if (p < nfull) {
+        const int sb = p >> 8, q = p & 255;
+        const int x = q & 7, j = q >> 3;                  // XCD, slot on the XCD
+        const int nsbn = Nt / SBN;
+        const int sbm = sb / nsbn, sbn = sb % nsbn;
+        // XCD x takes sub-block (x + sb) % 8
+        const int s8 = (x + sb) & 7;
+        const int xm = s8 % (SBM / 8), xn = s8 / (SBM / 8);
+        mt = sbm * SBM + xm * 8 + (j & 7);
+        nt = sbn * SBN + xn * 4 + (j >> 3);
+        return;
+    }
+    const int q = p - nfull, rem = real_mt - F * SBM;
+    if (Nt % 8 == 0) {
+        const int x = q & 7, j = q >> 3;
+        nt = 8 * (j / rem) + x;
+        mt = F * SBM + j % rem;
+    } else {
+        mt = F * SBM + q / Nt;
+        nt = q % Nt;
+    }
 }
+
+// The last (R mod ncu) tiles would leave most CUs idle in a final, ragged
+// round.  When they are at most half a round, each of them is cut along K into
+// S = ncu / tail slices (at most kMaxUnits slices in all, each at least NS
+// k-tiles deep): the slices form one full round and write fp32 partial tiles,
+// which ffn_gemm_fixup sums in slice order before the epilogue.
+constexpr int kMaxUnits = 256;
+
+struct TailPlan {
+    int real_mt;      // real row tiles
+    int full;         // tiles computed whole: positions [0, full)
+    int tail;         // tiles cut into S slices: positions [full, full + tail S)
+    int S;            // slices per tail tile (1: no cut)
+};
+
+template <int BM>
+__device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int Nt,
+                                              int ncu, int nk, bool allow) {
+    TailPlan pl;
+    const int mtiles = __builtin_amdgcn_readfirstlane(real_row_tiles<BM>(offsets, E));
+    pl.real_mt = mtiles;
+    const int R = mtiles * Nt;
+    pl.tail = R % ncu;
+    int S = pl.tail > 0 ? min(ncu, kMaxUnits) / pl.tail : 1;
+    S = min(S, nk / Cfg<BM>::NS);
+    if (!allow || S < 2) {
+        pl.S = 1;
+        pl.tail = 0;
+    } else {
+        pl.S = S;
+    }
+    pl.full = R - pl.tail;
+    return pl;
+}
+
+// Expert, row range and column offset of tile (mt, nt).
+struct TileRef {
+    int e, m0, row_begin, n_rows, n0;
+};
 
 // LDS layouts (per stage):
 //   weights [k][n]: 32 rows of 512 bytes; 16-byte chunk c of row k is stored
@@ -140,22 +227,14 @@ __device__ __forceinline__ void tile_coords(int b, int SBN, int nsbn, int nsbm, 
 //     c ^ ((m >> RSH) % CPR), RSH = log2(16 / CPR).
 // Both swizzles make every fragment read land in 16 distinct 16-byte bank
 // slots per 16 lanes; the DMA writes are 1 KB contiguous per instruction.
-template <int BM, int ACT>
-__global__ __launch_bounds__(256) void ffn_gemm_bf16(
-    const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
-    const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Mt, int Nt,
-    int SBN) {
+// DMA pipeline and MFMA loop over the k-tiles [kb, kb + nkr) of tile `tr`,
+// accumulating into acc (the caller zeroes it).  `lds` holds Cfg<BM>::LDS_BYTES.
+template <int BM>
+__device__ __forceinline__ void gemm_mainloop(
+    const TileRef& tr, int kb, int nkr, char* lds, const uint16_t* __restrict__ X,
+    uint32_t x_bytes, const int32_t* __restrict__ rowmap, const uint16_t* __restrict__ W, int K,
+    int N, f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM]) {
     using G = Cfg<BM>;
-    __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
-
-    int mt, nt;
-    tile_coords(blockIdx.x, SBN, (Nt + SBN - 1) / SBN, (Mt + 256 / SBN - 1) / (256 / SBN), mt, nt);
-    int e, m0, row_begin, n_rows;
-    if (nt >= Nt || mt >= Mt) return;
-    if (!find_tile<BM>(offsets, E, mt, e, m0, row_begin, n_rows)) return;
-    const int n0 = nt * G::BN;
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -163,14 +242,14 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     // ---- DMA sources (byte offsets; fixed for the whole k loop except + k0)
     const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(X, x_bytes);
     const __amdgpu_buffer_rsrc_t w_rsrc =
-        make_rsrc(W + (int64_t)e * K * N, (uint32_t)K * (uint32_t)N * 2u);
+        make_rsrc(W + (int64_t)tr.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
     uint32_t woff[G::WI];
 #pragma unroll
     for (int q = 0; q < G::WI; ++q) {
         const int blk = 4 * q + wave;                       // 1 KB block = 2 weight rows
         const int k = 2 * blk + (lane >> 5);
         const int c = (lane & 31) ^ (4 * (k & 3));           // logical 16-byte chunk
-        woff[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)(n0 + 8 * c) * 2u;
+        woff[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)(tr.n0 + 8 * c) * 2u;
     }
     uint32_t xoff[G::XI];
     int xk[G::XI];
@@ -179,20 +258,20 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         const int blk = 4 * q + wave;                       // 1 KB block = RPB rows
         const int row = G::RPB * blk + lane / G::CPR;
         const int c = (lane % G::CPR) ^ ((row >> G::RSH) % G::CPR);
-        const int r = row_begin + min(m0 + row, n_rows - 1);
+        const int r = tr.row_begin + min(tr.m0 + row, tr.n_rows - 1);
         const uint32_t src = rowmap ? (uint32_t)rowmap[r] : (uint32_t)r;
         xoff[q] = src * (uint32_t)K * 2u + (uint32_t)c * 16u;
         xk[q] = 8 * c;
     }
     const uint32_t wstep = (uint32_t)G::BK * (uint32_t)N * 2u;
 
-    // DMA number q (0 <= q < WI + XI) of k-tile t, into stage t % NS.  k-tiles
-    // past the end read at out-of-range offsets and fill the stage with zeros.
+    // DMA number q (0 <= q < WI + XI) of k-tile kb + t, into stage t % NS.
+    // k-tiles past K read at out-of-range offsets and fill the stage with zeros.
     auto issue_one = [&](int t, int q) {
         const uint32_t st = lds0 + (uint32_t)((t % G::NS) * G::STAGE);
-        const int k0 = t * G::BK;
+        const int k0 = (kb + t) * G::BK;
         if (q < G::WI) {
-            dma16(w_rsrc, woff[q] + (uint32_t)t * wstep,
+            dma16(w_rsrc, woff[q] + (uint32_t)(kb + t) * wstep,
                   __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024)));
         } else {
             const int qx = q - G::WI;
@@ -249,13 +328,6 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         for (int o = 0; o < G::FN + G::FM; ++o) read_frag(t, kk, buf, frag_id(o));
     };
 
-    f32x16_t acc[G::FN][G::FM];
-#pragma unroll
-    for (int i = 0; i < G::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < G::FM; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     // MFMAs number lo..hi-1 (row-major over the FN x FM accumulator tiles)
     auto mfma_range = [&](int buf, int lo, int hi) {
 #pragma unroll
@@ -282,7 +354,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     // the fragment reads of a substep go into its first half of MFMA groups,
     // so they land well before the next substep's first MFMA needs them
     constexpr int RG2 = H2 > 1 ? H2 / 2 : 1, RG1 = H1 > 1 ? H1 / 2 : 1;
-    const int nk = (K + G::BK - 1) / G::BK;
+    const int nk = nkr;
 #pragma unroll
     for (int t = 0; t + 1 < G::NS; ++t)
 #pragma unroll
@@ -359,7 +431,18 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
+}
 
+// Bias, activation, bf16 and the store of tile `tr` from the accumulators.
+template <int BM, int ACT>
+__device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
+                                              f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
+                                              char* lds, const uint16_t* __restrict__ bias,
+                                              uint16_t* __restrict__ C, int N) {
+    using G = Cfg<BM>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % G::WN, wm = wave / G::WN;
+    const int l32 = lane & 31, half = lane >> 5;
     // ---- epilogue.  D[n][m]: a lane owns m = l32 and n = 8 g + 4 half + 0..3 of
     // each 32x32 tile.  Bias and activation in fp32, one rounding to bf16, then
     // the whole output tile is staged in LDS ([m][n], 528-byte pitch: the
@@ -368,13 +451,13 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     // segments, so every 128-byte line of the output is written once.
     wait_lgkm0();
     lds_barrier();
-    const uint16_t* be = bias ? bias + (int64_t)e * N : nullptr;
+    const uint16_t* be = bias ? bias + (int64_t)tr.e * N : nullptr;
 #pragma unroll
     for (int i = 0; i < G::FN; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
-            const int n = min(n0 + nl, N - 4);
+            const int n = min(tr.n0 + nl, N - 4);
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if (be) {
                 const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(be + n);
@@ -400,14 +483,149 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         }
     }
     lds_barrier();
-    const int rows = min(G::BM_ROWS, n_rows - m0);
-    const int chunks = min(G::BN, N - n0) / 8;            // 16-byte chunks per row (N % 8 == 0)
-    uint16_t* cbase = C + (int64_t)(row_begin + m0) * N + n0;
+    const int rows = min(G::BM_ROWS, tr.n_rows - tr.m0);
+    const int chunks = min(G::BN, N - tr.n0) / 8;         // 16-byte chunks per row (N % 8 == 0)
+    uint16_t* cbase = C + (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
     for (int idx = tid; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
         const int r = idx / (G::BN / 8), c = idx % (G::BN / 8);
         if (r < rows && c < chunks)
             *reinterpret_cast<u32x4_t*>(cbase + (int64_t)r * N + c * 8) =
                 *reinterpret_cast<const u32x4_t*>(lds + r * G::OP + c * 16);
+    }
+}
+
+// fp32 partial tile of one K slice, lane-major so every access is a 16-byte
+// vector: [wave][i][j][r / 4][lane][r % 4] (r / 4 is the epilogue's column
+// group g), Cfg<BM>::UNIT floats per slice.
+template <int BM>
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
+                                              float* __restrict__ dst) {
+    using G = Cfg<BM>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    f32x4_t* p = reinterpret_cast<f32x4_t*>(dst + (int64_t)wave * (G::UNIT / 4));
+#pragma unroll
+    for (int i = 0; i < G::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < G::FM; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4_t v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                                   acc[i][j][4 * r4 + 3]};
+                p[((i * G::FM + j) * 4 + r4) * 64 + lane] = v;
+            }
+}
+
+template <int BM>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM]) {
+#pragma unroll
+    for (int i = 0; i < Cfg<BM>::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg<BM>::FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+template <int BM>
+__device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, int E, int mt,
+                                         int nt, TileRef& tr) {
+    tr.n0 = nt * Cfg<BM>::BN;
+    return find_tile<BM>(offsets, E, mt, tr.e, tr.m0, tr.row_begin, tr.n_rows);
+}
+
+// Workgroup p: whole tile p (p < full), or one K slice of a tail tile.  `part`
+// (nullable) is the fp32 slice buffer; without it no tile is cut.
+template <int BM, int ACT>
+__global__ __launch_bounds__(256) void ffn_gemm_bf16(
+    const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
+    const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Nt, int SBN,
+    int ncu, float* __restrict__ part) {
+    using G = Cfg<BM>;
+    __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
+    const int nk = (K + G::BK - 1) / G::BK;
+    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, part != nullptr);
+    const int p = blockIdx.x;
+    int tile = p, kb = 0, nkr = nk, unit = -1;
+    if (p >= pl.full) {
+        const int u = p - pl.full;
+        if (u >= pl.tail * pl.S) return;
+        tile = pl.full + u / pl.S;
+        const int s = u % pl.S;
+        kb = s * nk / pl.S;
+        nkr = (s + 1) * nk / pl.S - kb;
+        unit = u;
+    }
+    int mt, nt;
+    dense_coords(tile, pl.real_mt, Nt, SBN, mt, nt);
+    TileRef tr;
+    if (!tile_ref<BM>(offsets, E, mt, nt, tr)) return;
+    f32x16_t acc[G::FN][G::FM];
+    zero_acc<BM>(acc);
+    gemm_mainloop<BM>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
+    if (unit < 0)
+        gemm_epilogue<BM, ACT>(tr, acc, lds, bias, C, N);
+    else
+        store_partial<BM>(acc, part + (int64_t)unit * G::UNIT);
+}
+
+// Tail tiles: workgroup (tile i, chunk c) takes 1024 of the tile's 16-byte
+// partial vectors, one per thread: the S slices summed in slice order, then
+// bias, activation, one rounding to bf16 and an 8-byte store.  A vector
+// [wave][i][j][g][lane] holds columns 8 g + 4 (lane / 32) + 0..3 of row
+// lane % 32 in MFMA tile (i, j) of that wave, as in the epilogue.
+template <int BM>
+struct FixCfg {
+    static constexpr int VEC = Cfg<BM>::UNIT / 4;        // 16-byte vectors per tile
+    static constexpr int CHUNKS = VEC / 1024;            // workgroups per tile
+};
+
+template <int BM, int ACT>
+__global__ __launch_bounds__(256) void ffn_gemm_fixup(
+    const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ C, int K, int N, int Nt, int SBN, int ncu,
+    const float* __restrict__ part) {
+    using G = Cfg<BM>;
+    const int nk = (K + G::BK - 1) / G::BK;
+    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, true);
+    const int i = blockIdx.x / FixCfg<BM>::CHUNKS, c = blockIdx.x % FixCfg<BM>::CHUNKS;
+    if (pl.S < 2 || i >= pl.tail) return;
+    int mt, nt;
+    dense_coords(pl.full + i, pl.real_mt, Nt, SBN, mt, nt);
+    TileRef tr;
+    if (!tile_ref<BM>(offsets, E, mt, nt, tr)) return;
+    // vector index v within a slice: 4 such 1024-vector blocks per thread group
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int v = c * 1024 + it * 256 + (int)threadIdx.x;
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part) + (int64_t)i * pl.S * FixCfg<BM>::VEC + v;
+        f32x4_t a = src[0];
+        for (int s = 1; s < pl.S; ++s) {
+            const f32x4_t t = src[(int64_t)s * FixCfg<BM>::VEC];
+            a[0] += t[0]; a[1] += t[1]; a[2] += t[2]; a[3] += t[3];
+        }
+        // decode [wave][i][j][g][lane]
+        const int lane = v & 63, g = (v >> 6) & 3, ij = (v >> 8) % (G::FN * G::FM);
+        const int wave = (v >> 8) / (G::FN * G::FM);
+        const int fi = ij / G::FM, fj = ij % G::FM;
+        const int wn = wave % G::WN, wm = wave / G::WN;
+        const int ml = wm * G::TM + 32 * fj + (lane & 31);
+        const int nl = wn * G::TN + 32 * fi + 8 * g + 4 * (lane >> 5);
+        if (tr.m0 + ml >= tr.n_rows || tr.n0 + nl >= N) continue;
+        float o[4] = {a[0], a[1], a[2], a[3]};
+        if (bias) {
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + (int64_t)tr.e * N + tr.n0 + nl);
+            o[0] += bf16_lo(bb[0]);
+            o[1] += bf16_hi(bb[0]);
+            o[2] += bf16_lo(bb[1]);
+            o[3] += bf16_hi(bb[1]);
+        }
+        if (ACT == kActGelu)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = gelu_erf(o[q]);
+        u32x2_t w;
+        w[0] = pack_bf16x2(o[0], o[1]);
+        w[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2_t*>(C + (int64_t)(tr.row_begin + tr.m0 + ml) * N + tr.n0 + nl) = w;
     }
 }
 
@@ -489,23 +707,38 @@ int pick_bm(const moe_problem_t& p) {
     return 256;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
+    if (cus[d] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[d] = n;
+    }
+    return cus[d];
+}
+
+int gemm_nt(int N) { return (N + 255) / 256; }
+
 template <int ACT>
 hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* rowmap,
                        const int32_t* offsets, const void* W, const void* bias, void* Cout,
-                       int K, int N, hipStream_t s) {
+                       int K, int N, float* part, hipStream_t s) {
     const int64_t rows = p.T * p.k;
     if (p.dtype == MOE_DTYPE_BF16) {
         const int bm = pick_bm(p);
-        const int Mt = (int)((rows + bm - 1) / bm + p.E);
-        const int Nt = (N + 255) / 256;
+        const int Mt = (int)((rows + bm - 1) / bm + p.E);     // row tiles, worst case
+        const int Nt = gemm_nt(N);
         // super-block width in column tiles: the widest of 16/8/4 that divides Nt
-#ifdef MOE_GEMM_SBN
-        const int SBN = MOE_GEMM_SBN;
-#else
         const int SBN = (Nt % 16 == 0) ? 16 : (Nt % 8 == 0) ? 8 : 4;
-#endif
-        const int64_t nsb = (int64_t)((Mt + 256 / SBN - 1) / (256 / SBN)) * ((Nt + SBN - 1) / SBN);
-        const dim3 grid((unsigned)(nsb * 256)), block(256);
+        const int ncu = device_cus();
+        const int units = std::min(ncu, kMaxUnits);
+        // every real tile, plus room for one round of K slices
+        const dim3 grid((unsigned)((int64_t)Mt * Nt + units)), block(256);
         auto* x = static_cast<const uint16_t*>(X);
         auto* w = static_cast<const uint16_t*>(W);
         auto* b = static_cast<const uint16_t*>(bias);
@@ -513,12 +746,26 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         // bytes addressable through X: the token rows (gather) or the kept rows
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
-        if (bm == 256)
-            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
-        else if (bm == 128)
-            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
-        else
-            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN);
+        // tail tiles are at most units / 2 (every tail tile is cut in 2 or more)
+        if (bm == 256) {
+            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
+                                                          K, N, Nt, SBN, ncu, part);
+            if (part)
+                ffn_gemm_fixup<256, ACT><<<dim3((unsigned)(units / 2 * FixCfg<256>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
+                                                                SBN, ncu, part);
+        } else if (bm == 128) {
+            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
+                                                          K, N, Nt, SBN, ncu, part);
+            if (part)
+                ffn_gemm_fixup<128, ACT><<<dim3((unsigned)(units / 2 * FixCfg<128>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
+                                                                SBN, ncu, part);
+        } else {
+            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
+                                                         K, N, Nt, SBN, ncu, part);
+            if (part)
+                ffn_gemm_fixup<64, ACT><<<dim3((unsigned)(units / 2 * FixCfg<64>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
+                                                               SBN, ncu, part);
+        }
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
         const int Nt = (N + 63) / 64;
@@ -533,13 +780,19 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
 
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         hipStream_t s) {
-    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, s);
+                         float* part, hipStream_t s) {
+    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, s);
 }
 
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
-                           const void* W2, const void* b2, void* y, hipStream_t s) {
-    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, p.F, p.H, s);
+                           const void* W2, const void* b2, void* y, float* part, hipStream_t s) {
+    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, p.F, p.H, part, s);
+}
+
+size_t gemm_partial_bytes(const moe_problem_t& p) {
+    if (p.dtype != MOE_DTYPE_BF16) return 0;
+    // at most kMaxUnits K slices of one BM x 256 fp32 tile each
+    return (size_t)kMaxUnits * (size_t)pick_bm(p) * 256u * sizeof(float);
 }
 
 }  // namespace moe

@@ -36,6 +36,7 @@ WsLayout ws_layout(const moe_problem_t& p) {
     L.chunk_hist = take(nc * E * 4);
     L.chunk_base = take(nc * E * 4);
     L.col_tot = take(E * 4);
+    L.gemm_part = take(gemm_partial_bytes(p));
     L.permute_bytes = off;
     L.ffn_bytes = 0;
     L.logits = 0;                 // moe_forward never stores logits in the workspace
@@ -153,16 +154,18 @@ moe_status_t moe_permute(const moe_problem_t* p, const void* x, const int32_t* t
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_t* offsets,
                             const void* W1, const void* b1, const void* W2, const void* b2,
                             void* h, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (!xp || !offsets || !W1 || !W2 || !h || !y) return MOE_ERR_INVALID_ARG;
     if (!aligned16(xp) || !aligned16(offsets) || !aligned16(W1) || !opt_ok(b1) ||
         !aligned16(W2) || !opt_ok(b2) || !aligned16(h) || !aligned16(y))
         return MOE_ERR_UNSUPPORTED;
-    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, stream);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, stream);
+    // the workspace is optional here: with it, the ragged last round of tiles
+    // is cut along K (see moe_workspace_bytes)
+    float* part = (ws && aligned16(ws) && ws_bytes >= gemm_partial_bytes(*p))
+                      ? static_cast<float*>(ws) : nullptr;
+    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, part, stream);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, part, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -219,9 +222,10 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
         e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt, losses,
                            stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
-    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, stream);
+    float* part = reinterpret_cast<float*>(w + L.gemm_part);
+    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, part, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, stream);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, stream);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
     if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
     if (e == hipSuccess) e = ev(MOE_EV_END);

@@ -46,6 +46,7 @@ struct WsLayout {
     size_t chunk_hist;   // [E][nchunk] int32 expert histogram per chunk
     size_t chunk_base;   // [E][nchunk] int32 pairs routed to e before the chunk
     size_t col_tot;      // [E] int32: pairs routed to each expert
+    size_t gemm_part;    // fp32 K-slice partial tiles of the expert GEMMs' last round
     // moe_forward intermediates, used when the caller passes NULL
     size_t logits, topk_idx, topk_w, counts, offsets, pos, row_token, xp, h, y;
     size_t route_bytes, permute_bytes, ffn_bytes, total;
@@ -75,11 +76,14 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
                           float* fin_losses, hipStream_t s);
 // rowmap (nullable): when set, row r of the first GEMM reads x[rowmap[r]]
 // instead of xp[r] (the gather fused into the operand load).
+// part (nullable): fp32 buffer of gemm_partial_bytes(p) for the K slices of
+// the ragged last round of tiles; without it no tile is cut.
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         hipStream_t s);
+                         float* part, hipStream_t s);
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
-                           const void* W2, const void* b2, void* y, hipStream_t s);
+                           const void* W2, const void* b2, void* y, float* part, hipStream_t s);
+size_t gemm_partial_bytes(const moe_problem_t& p);
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s);
 

@@ -212,6 +212,62 @@ def test_expert_ffn_stage(spec):
     assert_close_storage(as_f64(y[:A]), y_ref, spec.dtype, "y")
 
 
+def _tail_plan_host(offsets, bm, nt, ncu, nk, ns=4, max_units=256):
+    """Host copy of the rule the GEMM applies on the device: the real tiles'
+    ragged last round (R mod ncu tiles) is cut into S K-slices when S >= 2."""
+    mt = sum((int(offsets[e + 1]) - int(offsets[e]) + bm - 1) // bm for e in range(len(offsets) - 1))
+    tail = (mt * nt) % ncu
+    S = min(ncu, max_units) // tail if tail else 1
+    S = min(S, nk // ns)
+    return (tail, S) if S >= 2 else (0, 1)
+
+
+SPLIT = S("split_T4096_H512_E8_k2_F2048", 4096, 512, 8, 2, 2048)
+
+
+def test_expert_ffn_tail_split():
+    """With a workspace, the last round of tiles is cut along K (fp32 partials
+    summed in slice order); the result must match the oracle like whole tiles
+    do.  At this shape the up GEMM cuts 40 of ~296 tiles and the down GEMM
+    cuts all of its ~74 tiles (no whole tile at all)."""
+    spec = SPLIT
+    say(f"[expert_ffn tail split] {spec.name}")
+    inp = W.generate(spec)
+    ref = om.route(spec, om.logits(spec, inp["x"], inp["Wg"], inp["bg"]))
+    dsp = om.dispatch(spec, ref["topk_idx"])
+    off_h = dsp["offsets"]
+    A = int(off_h[-1])
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    up = _tail_plan_host(off_h, 256, (spec.F + 255) // 256, ncu, spec.H // 32)
+    down = _tail_plan_host(off_h, 256, (spec.H + 255) // 256, ncu, spec.F // 32)
+    say(f"    tail plan on {ncu} CUs: up {up}, down {down}")
+    assert up[1] >= 2 and down[1] >= 2, "shape no longer exercises the K split"
+    rows = inp["x"][dsp["row_token"][:A]]
+    experts = np.repeat(np.arange(spec.E), np.diff(off_h))
+    h_ref, y_ref = om.expert_rows(spec, rows, experts, inp["W1"], inp.get("b1"), inp["W2"],
+                                  inp.get("b2"))
+    prob = moe.Problem.from_spec(spec)
+    d = upload(spec, inp)
+    T, k = spec.T, spec.k
+    xp = torch.zeros(T * k, spec.H, dtype=storage_dtype(spec), device=DEV)
+    xp[:A] = dev(rows, spec.dtype)
+    off = dev(off_h, "i32")
+    outs = {}
+    for tag, ws in (("split", workspace(prob)), ("whole", None)):
+        h = torch.empty(T * k, spec.F, dtype=storage_dtype(spec), device=DEV)
+        y = torch.empty(T * k, spec.H, dtype=storage_dtype(spec), device=DEV)
+        moe.moe_expert_ffn(prob, xp, off, d["W1"], d.get("b1"), d["W2"], d.get("b2"), h, y, ws)
+        torch.cuda.synchronize()
+        assert_close_storage(as_f64(h[:A]), h_ref, spec.dtype, f"h ({tag})")
+        assert_close_storage(as_f64(y[:A]), y_ref, spec.dtype, f"y ({tag})")
+        outs[tag] = (h[:A].clone(), y[:A].clone())
+    # the two differ only in fp32 summation order inside the cut tiles
+    for a, b, nm in ((outs["split"][0], outs["whole"][0], "h"), (outs["split"][1], outs["whole"][1], "y")):
+        diff = (a.float() - b.float()).abs()
+        scale = b.float().abs().clamp_min(float(b.float().pow(2).mean().sqrt()))
+        assert float((diff / scale).max()) <= 2.0 ** -6, f"{nm}: split and whole tiles disagree"
+
+
 @pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[3], SMALL[8]], ids=lambda s: s.name)
 def test_combine_stage(spec):
     say(f"[combine] {spec.name}")
