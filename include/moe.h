@@ -31,7 +31,9 @@
  *   Device faults are asynchronous and surface at the caller's next
  *   synchronisation, as with any stream API.  No C++ exception crosses the ABI.
  * - Kernel envelope: 1 <= E <= 256, 1 <= k <= min(E, 8), T * k < 2^31,
- *   H and F multiples of 8 (bf16) or 4 (fp32), every pointer 16-byte aligned.
+ *   H and F multiples of 8 (bf16) or 4 (fp32), every pointer 16-byte aligned;
+ *   for bf16 also T*H*2, H*F*2 and E*H*2 below 2^31 bytes (the 32-bit ranges
+ *   of the gathered token rows, one expert's weight block and the gate).
  *   Outside it a call returns MOE_ERR_UNSUPPORTED.
  *
  * Determinism: no floating-point atomics are used; repeated calls on the same

@@ -239,8 +239,14 @@ __device__ __forceinline__ void gemm_mainloop(
     const int wn = wave % G::WN, wm = wave / G::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-    // ---- DMA sources (byte offsets; fixed for the whole k loop except + k0)
-    const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(X, x_bytes);
+    // ---- DMA sources (byte offsets; fixed for the whole k loop except + k0).
+    // Contiguous rows: the resource starts at the tile's first row, so only one
+    // tile has to fit the 32-bit offsets.  Gathered rows (rowmap): it spans X.
+    const int tile_rows = min(BM, tr.n_rows - tr.m0);
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        rowmap ? make_rsrc(X, x_bytes)
+               : make_rsrc(X + (int64_t)(tr.row_begin + tr.m0) * K,
+                           (uint32_t)tile_rows * (uint32_t)K * 2u);
     const __amdgpu_buffer_rsrc_t w_rsrc =
         make_rsrc(W + (int64_t)tr.e * K * N, (uint32_t)K * (uint32_t)N * 2u);
     uint32_t woff[G::WI];
@@ -258,8 +264,9 @@ __device__ __forceinline__ void gemm_mainloop(
         const int blk = 4 * q + wave;                       // 1 KB block = RPB rows
         const int row = G::RPB * blk + lane / G::CPR;
         const int c = (lane % G::CPR) ^ ((row >> G::RSH) % G::CPR);
-        const int r = tr.row_begin + min(tr.m0 + row, tr.n_rows - 1);
-        const uint32_t src = rowmap ? (uint32_t)rowmap[r] : (uint32_t)r;
+        const int rr = min(row, tile_rows - 1);             // row within the tile
+        const uint32_t src =
+            rowmap ? (uint32_t)rowmap[tr.row_begin + tr.m0 + rr] : (uint32_t)rr;
         xoff[q] = src * (uint32_t)K * 2u + (uint32_t)c * 16u;
         xk[q] = 8 * c;
     }

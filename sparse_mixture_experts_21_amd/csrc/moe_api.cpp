@@ -1,6 +1,7 @@
 // C ABI of libmoe.so: argument validation, capacity, workspace layout and the
 // launch sequence of every stage.  All validation happens before the first
 // HIP call, so a rejected call enqueues nothing (and needs no GPU).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -73,6 +74,17 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->T > (int64_t)0x7fffffff / p->k) return MOE_ERR_UNSUPPORTED;
     const int vec = p->dtype == MOE_DTYPE_BF16 ? 8 : 4;
     if (p->H % vec != 0 || p->F % vec != 0) return MOE_ERR_UNSUPPORTED;
+    if (p->dtype == MOE_DTYPE_BF16) {
+        // 32-bit buffer-resource ranges (offsets at or past 2^31 mean "out of
+        // range"): the token rows the first GEMM gathers from, one expert's
+        // weight block, the gate, and the GEMM's tile grid.
+        const int64_t lim = (int64_t)1 << 31;
+        if (p->T * p->H * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+        if ((int64_t)p->H * p->F * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+        if ((int64_t)p->E * p->H * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+        const int64_t tiles = (p->T * p->k / 64 + p->E + 1) * (((int64_t)std::max(p->H, p->F) + 255) / 256);
+        if (tiles + 256 >= lim) return MOE_ERR_UNSUPPORTED;
+    }
     return MOE_OK;
 }
 

@@ -87,7 +87,24 @@ BAD_PROBLEMS = [
     (dict(F=68), moe.MOE_ERR_UNSUPPORTED),
     (dict(H=34, dtype="f32"), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 30, k=2), moe.MOE_ERR_UNSUPPORTED),
+    # bf16: 32-bit buffer-resource ranges (gathered token rows, one expert's
+    # weights, the gate) must stay below 2^31 bytes
+    (dict(T=2 ** 18, H=4096), moe.MOE_ERR_UNSUPPORTED),
+    (dict(H=32768, F=32768), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=256, k=2, H=2 ** 22, F=8), moe.MOE_ERR_UNSUPPORTED),
 ]
+
+
+@pytest.mark.parametrize("kw", [dict(T=2 ** 18 - 1, H=4096), dict(H=32768, F=32760),
+                                dict(T=2 ** 18, H=4096, dtype="f32")])
+def test_range_envelope_edges_accepted(kw):
+    """Just inside the bf16 32-bit ranges, and fp32 (no such range): accepted
+    by the host-only queries."""
+    p = P(**kw)
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == moe.MOE_OK
+    cap = ctypes.c_int64()
+    assert moe.lib().moe_capacity(ctypes.byref(p), ctypes.byref(cap)) == moe.MOE_OK
 
 
 @pytest.mark.parametrize("kw,status", BAD_PROBLEMS, ids=[str(b[0]) for b in BAD_PROBLEMS])
