@@ -539,8 +539,25 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
     return find_tile<BM>(offsets, E, mt, tr.e, tr.m0, tr.row_begin, tr.n_rows);
 }
 
+// One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
+template <int TB, int ACT>
+__device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
+                                           const uint16_t* __restrict__ X, uint32_t x_bytes,
+                                           const int32_t* __restrict__ rowmap,
+                                           const uint16_t* __restrict__ W,
+                                           const uint16_t* __restrict__ bias,
+                                           uint16_t* __restrict__ C, int K, int N) {
+    f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
+    zero_acc<TB>(acc);
+    gemm_mainloop<TB>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_epilogue<TB, ACT>(tr, acc, lds, bias, C, N);
+}
+
 // Workgroup p: whole tile p (p < full), or one K slice of a tail tile.  `part`
-// (nullable) is the fp32 slice buffer; without it no tile is cut.
+// (nullable) is the fp32 slice buffer; without it no tile is cut.  The last
+// row tile of an expert is usually short: with at most 128 (64) real rows it
+// runs the 128-row (64-row) layout, whose four waves split the columns instead
+// of idling on rows that do not exist.
 template <int BM, int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
@@ -566,13 +583,27 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     dense_coords(tile, pl.real_mt, Nt, SBN, mt, nt);
     TileRef tr;
     if (!tile_ref<BM>(offsets, E, mt, nt, tr)) return;
+    if (unit < 0) {
+        const int rows = tr.n_rows - tr.m0;
+        if constexpr (BM >= 128) {
+            if (rows <= 64) {
+                whole_tile<64, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                return;
+            }
+        }
+        if constexpr (BM >= 256) {
+            if (rows <= 128) {
+                whole_tile<128, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                return;
+            }
+        }
+        whole_tile<BM, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+        return;
+    }
     f32x16_t acc[G::FN][G::FM];
     zero_acc<BM>(acc);
     gemm_mainloop<BM>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
-    if (unit < 0)
-        gemm_epilogue<BM, ACT>(tr, acc, lds, bias, C, N);
-    else
-        store_partial<BM>(acc, part + (int64_t)unit * G::UNIT);
+    store_partial<BM>(acc, part + (int64_t)unit * G::UNIT);
 }
 
 // Tail tiles: workgroup (tile i, chunk c) takes 1024 of the tile's 16-byte
