@@ -36,21 +36,25 @@ namespace {
 
 enum Act { kActNone = 0, kActGelu = 1 };
 
-// Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)), with erf evaluated by formula
-// 7.1.26 of Abramowitz & Stegun, Handbook of Mathematical Functions:
+// Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)) = max(a, 0) - 0.5 |a| q with
+// q = 1 - erf(|a| / sqrt 2) (erf is odd; no cancellation for a < 0, where the
+// result is the small 0.5 a q), erf evaluated by formula 7.1.26 of Abramowitz & Stegun,
+// Handbook of Mathematical Functions:
 //   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
 //   t = 1 / (1 + p u), u >= 0, |error| <= 1.5e-7,
-// i.e. below fp32 rounding of GELU's output scale and far below bf16.  One
-// reciprocal and one exponential, no branches.
+// i.e. below fp32 rounding of GELU's output scale and far below bf16.  With
+// u = |a| / sqrt 2 the factor 1/sqrt 2 folds into p, and exp(-u^2) is
+// 2^(a^2 * (-1 / (2 ln 2))).  One reciprocal and one exponential, no branches.
 __device__ __forceinline__ float gelu_erf(float a) {
-    const float u = fabsf(a) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    const float aa = fabsf(a);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
     float poly = fmaf(t, 1.061405429f, -1.453152027f);
     poly = fmaf(t, poly, 1.421413741f);
     poly = fmaf(t, poly, -0.284496736f);
     poly = fmaf(t, poly, 0.254829592f);
-    const float q = t * poly * __expf(-u * u);          // 1 - erf(|a| / sqrt 2)
-    return 0.5f * a * ((a >= 0.0f) ? 2.0f - q : q);
+    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
+    const float q = t * poly * ex;                        // 1 - erf(|a| / sqrt 2)
+    return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
 }
 
 // Locate the expert and row tile of row-tile index mt.  Returns false when mt
