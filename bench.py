@@ -155,11 +155,91 @@ def cpu_baseline(spec, inp, target_s: float):
     t_ffn = ffn(n) if n > n0 else t_probe
     per_tok = t_ffn / n
     total = t_route + per_tok * spec.T
+    kept = int((dsp["pos"][:n] >= 0).sum())                 # kept pairs of the sample
+    flops = 2.0 * spec.T * spec.H * spec.E + 4.0 * spec.H * spec.F * kept
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": spec.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu, "gflops": flops / (t_route + t_ffn) / 1e9,
             "sample": (f"fp64 C oracle, {threads} OpenMP threads: gate/softmax/top-k/losses/"
                        f"dispatch over all {spec.T} tokens ({t_route:.2f} s) + expert FFN and "
                        f"combine on tokens 0..{n - 1} ({t_ffn:.2f} s), FFN time scaled "
                        f"linearly to {spec.T} tokens")}
+
+
+def stage_timing(moe, torch, spec, prob, d, log_fn, min_iters=50, min_seconds=0.5):
+    """Every ABI call timed alone with HIP events on the caller's stream: 10
+    warm-ups, then at least `min_iters` iterations and `min_seconds`; warm
+    (back-to-back) and cold (a 512 MiB buffer written before every iteration,
+    which flushes the 256 MB last-level cache).  Returns ms quantiles and the
+    kept-row count A."""
+    import numpy as np
+    T, H, E, k, F = spec.T, spec.H, spec.E, spec.k, spec.F
+    sd = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    cu = "cuda"
+    ws = torch.empty(moe.moe_workspace_bytes(prob), dtype=torch.uint8, device=cu)
+    out = torch.empty(T, H, dtype=sd, device=cu)
+    losses = torch.empty(2, dtype=torch.float32, device=cu)
+    idx = torch.empty(T, k, dtype=torch.int32, device=cu)
+    tw = torch.empty(T, k, dtype=torch.float32, device=cu)
+    counts = torch.empty(E, dtype=torch.int32, device=cu)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=cu)
+    pos = torch.empty(T, k, dtype=torch.int32, device=cu)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=cu)
+    xp = torch.empty(T * k, H, dtype=sd, device=cu)
+    h = torch.empty(T * k, F, dtype=sd, device=cu)
+    y = torch.empty(T * k, H, dtype=sd, device=cu)
+    calls = {
+        "forward": lambda: moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"],
+                                           d["W2"], d["b2"], out, losses, ws),
+        "route": lambda: moe.moe_route(prob, d["x"], d["Wg"], d["bg"], None, idx, tw, counts,
+                                       losses, ws),
+        "permute": lambda: moe.moe_permute(prob, d["x"], idx, offsets, pos, row_token, xp, ws),
+        "expert_ffn": lambda: moe.moe_expert_ffn(prob, xp, offsets, d["W1"], d["b1"], d["W2"],
+                                                 d["b2"], h, y, ws),
+        "combine": lambda: moe.moe_combine(prob, y, pos, tw, out),
+    }
+    for name in ("route", "permute", "expert_ffn", "combine"):   # inputs of the later stages
+        calls[name]()
+    torch.cuda.synchronize()
+    A = int(offsets[-1].item())
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=cu)
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        est = (time.perf_counter() - t1) / 3
+        n = max(min_iters, int(min_seconds / max(est, 1e-6)) + 1)
+        row = {}
+        for mode in ("warm", "cold"):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for a, b in evs:
+                if mode == "cold":
+                    flush.fill_(1)
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in evs])
+            row[mode] = {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+                         "p90": float(np.percentile(ms, 90)), "n": n}
+        res[name] = row
+        log_fn(f"[bench] {name}: warm {row['warm']['median']:.4f} ms, cold {row['cold']['median']:.4f} ms")
+    del flush
+    return res, A
 
 
 def main():
@@ -238,6 +318,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    log("[bench] timing each ABI call alone (warm and cold)")
+    abi, A_abi = stage_timing(moe, torch, spec, prob, d, log)
     stage = np.array([ev.stage_ms() for ev in evs])          # [steps][5]
     stage_mean = stage.mean(axis=0)
     A = int(offsets[-1].item())
@@ -285,6 +367,17 @@ def main():
         "ffn_frac_of_bf16_peak": ffn_tflops / PEAK_BF16_TFLOPS,
         "stage_ms": sm,
         "hbm_stages": hbm,
+        "abi_ms": abi,
+        "abi_ffn_tflops": {m: 4.0 * H * F * A_abi / (abi["expert_ffn"][m]["median"] * 1e-3) / 1e12
+                           for m in ("warm", "cold")},
+        "abi_hbm_frac_cold": {
+            "route": (T * H * s + H * E * s + T * k * 8) / (abi["route"]["cold"]["median"] * 1e-3)
+                     / 1e9 / PEAK_HBM_GBS,
+            "permute": (T * k * 4 + T * H * s + A_abi * H * s + 2 * A_abi * 4)
+                       / (abi["permute"]["cold"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "combine": (A_abi * H * s + T * k * 8 + T * H * s)
+                       / (abi["combine"]["cold"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        },
         "losses": [float(v) for v in losses.cpu().numpy()],
     }
     if not args.no_cpu_baseline:

@@ -19,8 +19,8 @@
 //                   with 8 ballots over the expert id bits, and the rank is
 //                   the running per-expert count plus the number of matching
 //                   lower lanes;  pos = offsets[e] + rank when rank < cap;
-//   4. gather_rows  xp[r] = x[row_token[r]] with 16-byte copies (skipped when
-//                   the first expert GEMM reads x through row_token itself).
+//   4. gather_tokens  xp[pos[t][s]] = x[t], one workgroup per token (skipped
+//                   when the first expert GEMM reads x through row_token itself).
 #include "moe_internal.h"
 #include "route_finalize.h"
 
@@ -187,20 +187,36 @@ __global__ __launch_bounds__(64) void chunk_rank(const int32_t* __restrict__ top
     }
 }
 
-// xp[r] = x[row_token[r]] for r < offsets[E]; `vec` 16-byte vectors per row.
-__global__ __launch_bounds__(256) void gather_rows(const u32x4_t* __restrict__ x,
-                                                   const int32_t* __restrict__ row_token,
-                                                   const int32_t* __restrict__ offsets, int E,
-                                                   int64_t vec, int64_t rows_per_block,
-                                                   u32x4_t* __restrict__ xp) {
-    const int64_t A = offsets[E];
-    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-    if (r0 >= A) return;
-    const int64_t r1 = min(r0 + rows_per_block, A);
-    for (int64_t r = r0; r < r1; ++r) {
-        const u32x4_t* src = x + (int64_t)row_token[r] * vec;
-        u32x4_t* dst = xp + r * vec;
-        for (int64_t v = threadIdx.x; v < vec; v += 256) dst[v] = src[v];
+// xp[pos[t][s]] = x[t] for every kept slot: one workgroup per token, whose
+// destination rows are workgroup-uniform, so each x row is read exactly once
+// and each kept row written once (the minimum traffic), both nontemporally.
+constexpr int kGatherThreads = 256;
+constexpr int kGatherVec = 4;          // 16-byte vectors per thread and pass
+
+__global__ __launch_bounds__(kGatherThreads) void gather_tokens(
+    const u32x4_t* __restrict__ x, const int32_t* __restrict__ pos, int k, int64_t vec,
+    u32x4_t* __restrict__ xp) {
+    const int64_t t = blockIdx.x;
+    int32_t dst[kMaxK];
+#pragma unroll
+    for (int s = 0; s < kMaxK; ++s) dst[s] = s < k ? pos[t * k + s] : -1;
+    const u32x4_t* src = x + t * vec;
+    for (int64_t v0 = threadIdx.x; v0 < vec; v0 += kGatherThreads * kGatherVec) {
+        u32x4_t d[kGatherVec];
+#pragma unroll
+        for (int u = 0; u < kGatherVec; ++u) {
+            const int64_t v = v0 + (int64_t)u * kGatherThreads;
+            if (v < vec) d[u] = __builtin_nontemporal_load(&src[v]);
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            if (dst[s] < 0) continue;                  // uniform: dropped or past k
+#pragma unroll
+            for (int u = 0; u < kGatherVec; ++u) {
+                const int64_t v = v0 + (int64_t)u * kGatherThreads;
+                if (v < vec) __builtin_nontemporal_store(d[u], &xp[(int64_t)dst[s] * vec + v]);
+            }
+        }
     }
 }
 
@@ -239,12 +255,8 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
     }
     if (xp) {
         const int64_t row_bytes = (int64_t)p.H * (p.dtype == MOE_DTYPE_BF16 ? 2 : 4);
-        const int64_t vec = row_bytes / 16;
-        const int64_t rpb = vec >= 256 ? 4 : 16;
-        const int64_t nb = (T * k + rpb - 1) / rpb;
-        gather_rows<<<dim3((unsigned)nb), dim3(256), 0, s>>>(
-            static_cast<const u32x4_t*>(x), row_token, offsets, E, vec, rpb,
-            static_cast<u32x4_t*>(xp));
+        gather_tokens<<<dim3((unsigned)T), dim3(kGatherThreads), 0, s>>>(
+            static_cast<const u32x4_t*>(x), pos, k, row_bytes / 16, static_cast<u32x4_t*>(xp));
     }
     return hipGetLastError();
 }
