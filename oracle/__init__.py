@@ -27,7 +27,7 @@ _LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(HERE, "liboracle.so
 class _Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("cf", ctypes.c_double),
-                ("dtype", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("act", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,11 +58,14 @@ def lib():
 
 def problem(spec, **over) -> _Problem:
     """Build the oracle's problem struct from an inputs.Spec (fields T, H, E, k,
-    F, cf, dtype), with optional overrides."""
+    F, cf, dtype, act), with optional overrides."""
     g = lambda n: over.get(n, getattr(spec, n))
+    act = g("act")
+    if act not in ("gelu", "silu"):
+        raise ValueError(f"activation {act!r}")
     return _Problem(T=int(g("T")), H=int(g("H")), E=int(g("E")), k=int(g("k")),
                     F=int(g("F")), cf=float(g("cf")),
-                    dtype=1 if g("dtype") == "bf16" else 0, pad_=0)
+                    dtype=1 if g("dtype") == "bf16" else 0, act=1 if act == "silu" else 0)
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -19,8 +19,12 @@ mismatch:
   one boolean row mask per expert (no capacity limit).
 * ``torch_expert_major`` — the expert-major formulation of the page's Mixtral
   block (Advanced Patterns, Mixtral 8x7B Architecture): per-expert gather of
-  the (token, slot) pairs and ``index_add_`` back into token rows, with the
-  GELU experts and biases of the reference layer (no capacity limit).
+  the (token, slot) pairs and ``index_add_`` back into token rows (no
+  capacity limit).
+
+All three follow ``spec.act``: ``nn.GELU`` (exact erf) as in the reference
+layer, or ``nn.SiLU`` as in the Mixtral block; the numpy route evaluates SiLU
+as ``a * expit(a)`` and GELU with ``scipy.special.erf``.
 """
 from __future__ import annotations
 
@@ -77,7 +81,10 @@ def dense_then_mask(spec, inp: Dict[str, Optional[np.ndarray]]) -> Dict[str, obj
     Y = np.empty((E, T, H))
     for e in range(E):
         a = x @ W1[e] + (0.0 if b1 is None else b1[e][None, :])
-        g = 0.5 * a * (1.0 + special.erf(a / np.sqrt(2.0)))
+        if spec.act == "silu":
+            g = a * special.expit(a)
+        else:
+            g = 0.5 * a * (1.0 + special.erf(a / np.sqrt(2.0)))
         Y[e] = g @ W2[e] + (0.0 if b2 is None else b2[e][None, :])
     sel = Y[idx, np.arange(T)[:, None], :]           # [T, k, H]
     coef = w * kept.reshape(T, k)
@@ -105,7 +112,8 @@ def _torch_modules(spec, inp):
                 l1.bias.copy_(b1[e])
             if b2 is not None:
                 l2.bias.copy_(b2[e])
-        experts.append(torch.nn.Sequential(l1, torch.nn.GELU(), l2))
+        act = torch.nn.SiLU() if spec.act == "silu" else torch.nn.GELU()
+        experts.append(torch.nn.Sequential(l1, act, l2))
     gate = torch.nn.Linear(spec.H, E, bias=bg is not None, dtype=torch.float64)
     with torch.no_grad():
         gate.weight.copy_(Wg.T)

@@ -51,6 +51,7 @@ static int valid(const orc_problem* p) {
     if (p->T < 1 || p->H < 1 || p->E < 1 || p->F < 1) return 0;
     if (p->k < 1 || p->k > p->E) return 0;
     if (p->dtype != 0 && p->dtype != 1) return 0;
+    if (p->act != 0 && p->act != 1) return 0;
     return 1;
 }
 
@@ -210,9 +211,10 @@ int orc_dispatch(const orc_problem* p, const int32_t* topk_idx, int32_t* offsets
     return 0;
 }
 
-/* One expert row: a = xr . W1[e] + b1[e];  g = GELU(a) with the exact erf
- * form 0.5 a (1 + erf(a / sqrt 2));  y = g . W2[e] + b2[e]
- * (Basic MoE Architecture: Linear(H, 4H) -> nn.GELU() -> Linear(4H, H)). */
+/* One expert row: a = xr . W1[e] + b1[e];  g = act(a);  y = g . W2[e] + b2[e]
+ * (Basic MoE Architecture: Linear(H, 4H) -> nn.GELU() -> Linear(4H, H)), act
+ * the exact erf GELU 0.5 a (1 + erf(a / sqrt 2)); or SiLU a / (1 + exp(-a))
+ * (nn.SiLU of the Mixtral block, Advanced Patterns, Mixtral 8x7B Architecture). */
 static void expert_row(const orc_problem* p, const double* xr, int e, const void* W1,
                        const void* b1, const void* W2, const void* b2, double* a,
                        double* y) {
@@ -221,7 +223,8 @@ static void expert_row(const orc_problem* p, const double* xr, int e, const void
     for (int i = 0; i < H; ++i) axpy_row(a, xr[i], W1, ((int64_t)e * H + i) * F, F, dt);
     for (int j = 0; j < F; ++j) {
         if (b1) a[j] += load(b1, (int64_t)e * F + j, dt);
-        a[j] = 0.5 * a[j] * (1.0 + erf(a[j] * M_SQRT1_2));
+        a[j] = p->act == 1 ? a[j] / (1.0 + exp(-a[j]))
+                           : 0.5 * a[j] * (1.0 + erf(a[j] * M_SQRT1_2));
     }
     for (int o = 0; o < H; ++o) y[o] = 0.0;
     for (int j = 0; j < F; ++j) axpy_row(y, a[j], W2, ((int64_t)e * F + j) * H, H, dt);

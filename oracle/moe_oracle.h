@@ -7,7 +7,9 @@
  * It is a plain, slow, per-token fp64 implementation of the layer described
  * by the "moe-training" SKILL page (Quick Start, Basic MoE Architecture:
  * gate Linear -> softmax -> top-k -> renormalise -> per-expert
- * Linear(H,4H) -> GELU -> Linear(4H,H) -> weighted sum) together with the
+ * Linear(H,4H) -> GELU -> Linear(4H,H) -> weighted sum; or SiLU in place of
+ * GELU, as in the Mixtral block of Advanced Patterns, Mixtral 8x7B
+ * Architecture) together with the
  * load-balancing and router z-losses (Core Concepts, 3. Load Balancing) and
  * capacity-factor dropping (Core Concepts, 4. Expert Parallelism; Best
  * Practices, 2. Capacity Factor Tuning).
@@ -35,7 +37,7 @@ typedef struct {
     int32_t F;      /* expert inner width (4H on the pages) */
     double  cf;     /* capacity factor; <= 0 means no capacity limit */
     int32_t dtype;  /* 0: fp32 storage, 1: bf16 storage */
-    int32_t pad_;
+    int32_t act;    /* expert activation: 0 exact GELU, 1 SiLU */
 } orc_problem;
 
 /* Gate logits l[t][e] = bg[e] + sum_i x[t][i] * Wg[i][e]  (double, [T][E]). */

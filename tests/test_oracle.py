@@ -59,6 +59,8 @@ BRUTE_CASES = [
     dict(biases=False),
     dict(E=1, k=1),
     dict(T=1),
+    dict(act="silu"),
+    dict(act="silu", dtype="bf16", biases=False, E=8, k=2, T=40),
 ]
 
 
@@ -109,8 +111,9 @@ def test_oracle_combine_matches_indexing(oracle_mod):
 
 
 # ---------------------------------------------------------------- torch formulations
-def test_oracle_matches_torch_layers_on_tiny_fp32_config(oracle_mod):
-    spec = W.CONFIGS["c1"]
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_oracle_matches_torch_layers_on_tiny_fp32_config(oracle_mod, act):
+    spec = W.CONFIGS["c1"].replace(act=act)
     inp = W.generate(spec)
     o = run_oracle(oracle_mod, spec, inp)
     assert oracle_mod.topk_margin(spec, o["logits"]) > 1e-9      # no ties: torch.topk is safe
@@ -194,14 +197,35 @@ def test_identical_experts_reduce_to_dense_ffn(oracle_mod, cf):
         assert (o["pos"] < 0).any()
 
 
-def test_single_expert_is_dense_ffn(oracle_mod):
-    spec = tiny(T=33, E=1, k=1)
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_single_expert_is_dense_ffn(oracle_mod, act):
+    spec = tiny(T=33, E=1, k=1, act=act)
     inp = W.generate(spec, workers=1)
     o = run_oracle(oracle_mod, spec, inp)
     assert np.all(o["topk_w"] == 1.0)
     np.testing.assert_allclose(o["out"], bf.dense_ffn(spec, inp, 0), rtol=RT, atol=1e-11)
     assert math.isclose(o["aux"], 1.0, rel_tol=1e-14)
     np.testing.assert_allclose(o["lse"], o["logits"][:, 0], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_scalar_expert_activation_values(oracle_mod, act):
+    """H = F = 1, one expert with unit weights and zero biases: the output is the
+    activation itself.  GELU(a) = a * Phi(a) and SiLU(a) = a / (1 + e^-a) at
+    points where both are known in closed form or from the normal table."""
+    a = np.array([0.0, 1.0, -2.0, 3.0], np.float32)
+    spec = tiny(T=4, H=1, E=1, k=1, F=1, biases=False, act=act)
+    one = np.ones((1, 1, 1), np.float32)
+    inp = dict(x=a[:, None].copy(), Wg=np.ones((1, 1), np.float32), bg=None,
+               W1=one, b1=None, W2=one.copy(), b2=None)
+    o = run_oracle(oracle_mod, spec, inp)
+    if act == "silu":
+        want = [0.0, 1.0 / (1.0 + math.exp(-1.0)), -2.0 / (1.0 + math.exp(2.0)),
+                3.0 / (1.0 + math.exp(-3.0))]
+    else:   # Phi(1) = 0.841344746..., Phi(-2) = 0.022750131..., Phi(3) = 0.998650101...
+        want = [0.0, 0.8413447460685429, -2.0 * 0.022750131948179195,
+                3.0 * 0.9986501019683699]
+    np.testing.assert_allclose(o["out"][:, 0], want, rtol=1e-14, atol=1e-15)
 
 
 def test_k_equals_E_is_soft_mixture(oracle_mod):

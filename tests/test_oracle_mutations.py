@@ -14,6 +14,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 # name -> (text in the oracle source, planted replacement)
 MUTANTS = {
     "drop_expert_bias2": ("y[o] += load(b2, (int64_t)e * H + o, dt);", "y[o] += 0.0;"),
+    "silu_evaluated_as_gelu": ("p->act == 1 ?", "p->act == 99 ?"),
+    "silu_wrong_sign": ("a[j] / (1.0 + exp(-a[j]))", "a[j] / (1.0 + exp(a[j]))"),
     "gelu_wrong_sign": ("(1.0 + erf(a[j] * M_SQRT1_2))", "(1.0 - erf(a[j] * M_SQRT1_2))"),
     "aux_without_E": ("*aux = (double)E * acc;", "*aux = acc;"),
     "tie_to_higher_index": ("if (best < 0 || l[e] > l[best]) best = e;",

@@ -67,6 +67,7 @@ class Spec:
     w2: Dist = Dist("normal", 0.02)
     b2: Optional[Dist] = None
     identical_experts: bool = False   # every expert gets expert 0's weights
+    act: str = "gelu"                 # expert activation: "gelu" (exact erf) or "silu"
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -95,6 +96,9 @@ CONFIGS: Dict[str, Spec] = {
                dtype="bf16", cf=0.0, seed=4, bg=Dist("zipf_log", 1.2)),
     "c5": Spec("mixtral_T16384_H4096_E8_k2_F14336_cf2.0", T=16384, H=4096, E=8, k=2,
                F=14336, dtype="bf16", cf=2.0, seed=5),
+    # the Mixtral block of the pages: bias-free, SiLU experts, no capacity
+    "c5s": Spec("mixtral_silu_T16384_H4096_E8_k2_F14336_dropless", T=16384, H=4096, E=8,
+                k=2, F=14336, dtype="bf16", cf=0.0, seed=6, act="silu"),
 }
 
 
