@@ -358,7 +358,7 @@ def main():
         "dtype": spec.dtype,
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": spec.name, "T": T, "H": H, "E": E, "k": k, "F": F,
-                   "capacity_factor": spec.cf, "kept_rows": A},
+                   "capacity_factor": spec.cf, "activation": spec.act, "kept_rows": A},
         "roofline": {"bound": "mfma", "kernel": kern, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS,

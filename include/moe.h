@@ -52,13 +52,21 @@ extern "C" {
 
 typedef enum {
     MOE_OK = 0,
-    MOE_ERR_INVALID_ARG = 1,  /* null required pointer, T<1, E<1, k<1, k>E, H<1, F<1, bad dtype */
+    MOE_ERR_INVALID_ARG = 1,  /* null required pointer, T<1, E<1, k<1, k>E, H<1, F<1, bad dtype or activation */
     MOE_ERR_UNSUPPORTED = 2,  /* valid, but outside the kernel envelope above */
     MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the call needs */
     MOE_ERR_HIP = 4           /* a HIP launch or event call failed */
 } moe_status_t;
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Activation between the two expert linears.  MOE_ACT_GELU is the exact
+ * (erf) GELU of the basic layer (Quick Start, Basic MoE Architecture);
+ * MOE_ACT_SILU, a * sigmoid(a), is the expert of the Mixtral 8x7B block
+ * (Advanced Patterns, Mixtral 8x7B Architecture), whose linears, gate
+ * included, carry no bias (pass NULL biases) and whose dispatch has no
+ * capacity limit (capacity_factor <= 0). */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SILU = 1 } moe_activation_t;
 
 typedef struct {
     int64_t T;               /* tokens (batch * sequence, flattened) */
@@ -68,7 +76,7 @@ typedef struct {
     int32_t F;               /* expert inner width (4H on the pages) */
     double capacity_factor;  /* <= 0: no capacity limit (capacity = T) */
     int32_t dtype;           /* moe_dtype_t */
-    int32_t reserved;        /* must be 0 */
+    int32_t activation;      /* moe_activation_t: the experts' activation */
 } moe_problem_t;
 
 /* moe_route flag: read `logits` as an input and skip the gate linear. */

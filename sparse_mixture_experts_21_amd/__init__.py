@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
 (MOE_EV_ROUTE, MOE_EV_PERMUTE, MOE_EV_FFN_UP, MOE_EV_FFN_DOWN, MOE_EV_COMBINE,
  MOE_EV_END, MOE_FORWARD_EVENTS) = range(7)
@@ -38,23 +39,26 @@ class MoeError(RuntimeError):
 
 
 class Problem(ctypes.Structure):
-    """moe_problem_t.  dtype may be given as "bf16"/"f32" or the enum value."""
+    """moe_problem_t.  dtype may be given as "bf16"/"f32" and activation as
+    "gelu"/"silu", or either as the enum value."""
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_double), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("activation", ctypes.c_int32)]
 
-    def __init__(self, T, H, E, k, F, capacity_factor=0.0, dtype="bf16", reserved=0):
+    def __init__(self, T, H, E, k, F, capacity_factor=0.0, dtype="bf16", activation="gelu"):
         if isinstance(dtype, str):
             dtype = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32}[dtype]
+        if isinstance(activation, str):
+            activation = {"gelu": MOE_ACT_GELU, "silu": MOE_ACT_SILU}[activation]
         super().__init__(int(T), int(H), int(E), int(k), int(F), float(capacity_factor),
-                         int(dtype), int(reserved))
+                         int(dtype), int(activation))
 
     @classmethod
     def from_spec(cls, spec, **over) -> "Problem":
         g = lambda n: over.get(n, getattr(spec, n))
         return cls(g("T"), g("H"), g("E"), g("k"), g("F"), over.get("cf", spec.cf),
-                   g("dtype"))
+                   g("dtype"), g("act"))
 
     @property
     def elem_bytes(self) -> int:
@@ -62,7 +66,8 @@ class Problem(ctypes.Structure):
 
     def __repr__(self):
         return (f"Problem(T={self.T}, H={self.H}, E={self.E}, k={self.k}, F={self.F}, "
-                f"cf={self.capacity_factor}, dtype={'bf16' if self.dtype else 'f32'})")
+                f"cf={self.capacity_factor}, dtype={'bf16' if self.dtype else 'f32'}, "
+                f"activation={'silu' if self.activation == MOE_ACT_SILU else 'gelu'})")
 
 
 _lib = None

@@ -3,9 +3,11 @@
 // -> GELU -> Linear(4H, H); the page's explainer on efficient training notes
 // that batched matmuls assume equal group sizes, which this kernel does not).
 //
-//   up:   h[r] = GELU(X[r] . W1[e] + b1[e])     (K = H, N = F)
+//   up:   h[r] = act(X[r] . W1[e] + b1[e])      (K = H, N = F)
 //   down: y[r] = h[r] . W2[e] + b2[e]           (K = F, N = H)
-// for the rows offsets[e] <= r < offsets[e+1] of every expert e.
+// for the rows offsets[e] <= r < offsets[e+1] of every expert e, with act the
+// exact GELU, or SiLU for the Mixtral 8x7B expert (same page, Advanced
+// Patterns: bias-free Linear -> SiLU -> Linear experts).
 //
 // Tiles never straddle experts and are never padded to capacity: the grid is
 // sized for the worst case (T k / BM + E row tiles) and each workgroup finds
@@ -34,7 +36,7 @@
 namespace moe {
 namespace {
 
-enum Act { kActNone = 0, kActGelu = 1 };
+enum Act { kActNone = 0, kActGelu = 1, kActSilu = 2 };
 
 // Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)) = max(a, 0) - 0.5 |a| q with
 // q = 1 - erf(|a| / sqrt 2) (erf is odd; no cancellation for a < 0, where the
@@ -55,6 +57,20 @@ __device__ __forceinline__ float gelu_erf(float a) {
     const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
     const float q = t * poly * ex;                        // 1 - erf(|a| / sqrt 2)
     return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
+}
+
+// SiLU, a * sigmoid(a) = a / (1 + e^-a) with e^-a = 2^(-a log2 e).  For very
+// negative a the denominator overflows to +inf and the result is -0; for very
+// positive a it is 1 and the result is a.
+__device__ __forceinline__ float silu(float a) {
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+    if constexpr (ACT == kActGelu) return gelu_erf(v);
+    else if constexpr (ACT == kActSilu) return silu(v);
+    else return v;
 }
 
 // Locate the expert and row tile of row-tile index mt.  Returns false when mt
@@ -483,8 +499,7 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v[q] = acc[i][j][4 * g + q] + bv[q];
-                    if (ACT == kActGelu) v[q] = gelu_erf(v[q]);
+                    v[q] = activate<ACT>(acc[i][j][4 * g + q] + bv[q]);
                 }
                 u32x2_t o;
                 o[0] = pack_bf16x2(v[0], v[1]);
@@ -661,9 +676,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
             o[2] += bf16_lo(bb[1]);
             o[3] += bf16_hi(bb[1]);
         }
-        if (ACT == kActGelu)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = gelu_erf(o[q]);
+        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(o[q]);
         u32x2_t w;
         w[0] = pack_bf16x2(o[0], o[1]);
         w[1] = pack_bf16x2(o[2], o[3]);
@@ -727,8 +741,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const float* __restrict__ X,
         for (int j = 0; j < 4; ++j) {
             const int n = n0 + tx * 4 + j;
             if (n >= N) continue;
-            float v = acc[i][j] + (bias ? bias[(int64_t)e * N + n] : 0.f);
-            if (ACT == kActGelu) v = gelu_erf(v);
+            const float v = activate<ACT>(acc[i][j] + (bias ? bias[(int64_t)e * N + n] : 0.f));
             C[(int64_t)(row_begin + m) * N + n] = v;
         }
     }
@@ -823,6 +836,8 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
                          float* part, hipStream_t s) {
+    if (p.activation == MOE_ACT_SILU)
+        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, s);
     return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, s);
 }
 

@@ -68,7 +68,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
     if (p->T < 1 || p->H < 1 || p->F < 1 || p->E < 1 || p->k < 1 || p->k > p->E)
         return MOE_ERR_INVALID_ARG;
     if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
-    if (p->reserved != 0) return MOE_ERR_INVALID_ARG;
+    if (p->activation != MOE_ACT_GELU && p->activation != MOE_ACT_SILU) return MOE_ERR_INVALID_ARG;
     if (std::isnan(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if (p->E > kMaxE || p->k > kMaxK) return MOE_ERR_UNSUPPORTED;
     if (p->T > (int64_t)0x7fffffff / p->k) return MOE_ERR_UNSUPPORTED;

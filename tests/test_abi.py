@@ -79,7 +79,8 @@ BAD_PROBLEMS = [
     (dict(k=0), moe.MOE_ERR_INVALID_ARG),
     (dict(k=9, E=8), moe.MOE_ERR_INVALID_ARG),
     (dict(dtype=7), moe.MOE_ERR_INVALID_ARG),
-    (dict(reserved=1), moe.MOE_ERR_INVALID_ARG),
+    (dict(activation=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(activation=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(capacity_factor=math.nan), moe.MOE_ERR_INVALID_ARG),
     (dict(E=257, k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=16, k=9), moe.MOE_ERR_UNSUPPORTED),
@@ -93,6 +94,21 @@ BAD_PROBLEMS = [
     (dict(H=32768, F=32768), moe.MOE_ERR_UNSUPPORTED),
     (dict(E=256, k=2, H=2 ** 22, F=8), moe.MOE_ERR_UNSUPPORTED),
 ]
+
+
+def test_problem_struct_layout_matches_header():
+    # moe_problem_t: int64 T, int32 H E k F, double capacity_factor, int32 dtype activation
+    assert ctypes.sizeof(moe.Problem) == 40
+    assert moe.Problem.capacity_factor.offset == 24
+    assert moe.Problem.dtype.offset == 32 and moe.Problem.activation.offset == 36
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", moe.MOE_ACT_SILU])
+def test_both_activations_accepted(act):
+    p = P(activation=act)
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == moe.MOE_OK
+    assert n.value > 0
 
 
 @pytest.mark.parametrize("kw", [dict(T=2 ** 18 - 1, H=4096), dict(H=32768, F=32760),

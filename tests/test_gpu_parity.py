@@ -62,7 +62,14 @@ SMALL = [
     S("bf16_T257_H64_E8_k2_F256", 257, 64, 8, 2, 256, cf=1.25),
     S("bf16_tiny_cf_T256_H64_E8_k2_F128_cf0.1", 256, 64, 8, 2, 128, cf=0.1),
     S("f32_k3_E5_T100_H32_F64", 100, 32, 5, 3, 64, dtype="f32", cf=0.75, biases=True),
+    # SiLU experts (the Mixtral 8x7B block: no biases, no capacity), then with
+    # biases, drops and a ragged width, and in fp32
+    S("silu_bf16_T2048_H512_E8_k2_F2048_dropless", 2048, 512, 8, 2, 2048, act="silu"),
+    S("silu_bf16_ragged_T777_H264_E6_k2_F776_cf1.0", 777, 264, 6, 2, 776, cf=1.0,
+      biases=True, act="silu"),
+    S("silu_f32_k2_E4_T100_H32_F64", 100, 32, 4, 2, 64, dtype="f32", biases=True, act="silu"),
 ]
+SILU = [s for s in SMALL if s.act == "silu"]
 
 
 def _small_ids():
@@ -94,7 +101,7 @@ def test_forward_small_all_outputs(spec):
         assert np.all(as_f64(o["out"])[dropped] == 0.0)
 
 
-@pytest.mark.parametrize("spec", SMALL[:8], ids=_small_ids()[:8])
+@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2], ids=lambda s: s.name)
 def test_stages_equal_forward_bitwise(spec):
     say(f"[stages == forward] {spec.name}")
     inp = W.generate(spec)
@@ -186,8 +193,8 @@ def test_permute_stage(spec):
     assert np.array_equal(xs, inp["x"][dsp["row_token"][:A]])
 
 
-@pytest.mark.parametrize("spec", [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[6], SMALL[7]],
-                         ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[6], SMALL[7]]
+                         + SILU, ids=lambda s: s.name)
 def test_expert_ffn_stage(spec):
     say(f"[expert_ffn] {spec.name}")
     inp = W.generate(spec)
@@ -225,12 +232,13 @@ def _tail_plan_host(offsets, bm, nt, ncu, nk, ns=4, max_units=256):
 SPLIT = S("split_T4096_H512_E8_k2_F2048", 4096, 512, 8, 2, 2048)
 
 
-def test_expert_ffn_tail_split():
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_expert_ffn_tail_split(act):
     """With a workspace, the last round of tiles is cut along K (fp32 partials
     summed in slice order); the result must match the oracle like whole tiles
     do.  At this shape the up GEMM cuts 40 of ~296 tiles and the down GEMM
     cuts all of its ~74 tiles (no whole tile at all)."""
-    spec = SPLIT
+    spec = SPLIT.replace(act=act, name=f"{SPLIT.name}_{act}")
     say(f"[expert_ffn tail split] {spec.name}")
     inp = W.generate(spec)
     ref = om.route(spec, om.logits(spec, inp["x"], inp["Wg"], inp["bg"]))
@@ -296,7 +304,7 @@ def _sample_tokens(spec, pos, n=48, seed=0):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-FULL = ["c2", "c3", "c4", "c5"]
+FULL = ["c2", "c3", "c4", "c5", "c5s"]
 
 
 @pytest.mark.parametrize("name", FULL + ["c2_cf1.0"])
