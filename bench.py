@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-abi-timing", action="store_true",
+                    help="skip the per-call warm/cold timing that follows the timed steps "
+                         "(thousands of extra launches; counter runs of the profiler omit it)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU work for the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -318,8 +321,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    log("[bench] timing each ABI call alone (warm and cold)")
-    abi, A_abi = stage_timing(moe, torch, spec, prob, d, log)
+    abi, A_abi = None, None
+    if not args.no_abi_timing:
+        log("[bench] timing each ABI call alone (warm and cold)")
+        abi, A_abi = stage_timing(moe, torch, spec, prob, d, log)
     stage = np.array([ev.stage_ms() for ev in evs])          # [steps][5]
     stage_mean = stage.mean(axis=0)
     A = int(offsets[-1].item())
@@ -368,9 +373,10 @@ def main():
         "stage_ms": sm,
         "hbm_stages": hbm,
         "abi_ms": abi,
-        "abi_ffn_tflops": {m: 4.0 * H * F * A_abi / (abi["expert_ffn"][m]["median"] * 1e-3) / 1e12
-                           for m in ("warm", "cold")},
-        "abi_hbm_frac_cold": {
+        "abi_ffn_tflops": None if abi is None else {
+            m: 4.0 * H * F * A_abi / (abi["expert_ffn"][m]["median"] * 1e-3) / 1e12
+            for m in ("warm", "cold")},
+        "abi_hbm_frac_cold": None if abi is None else {
             "route": (T * H * s + H * E * s + T * k * 8) / (abi["route"]["cold"]["median"] * 1e-3)
                      / 1e9 / PEAK_HBM_GBS,
             "permute": (T * k * 4 + T * H * s + A_abi * H * s + 2 * A_abi * 4)
