@@ -201,8 +201,10 @@ __device__ __forceinline__ void dense_coords(int p, int real_mt, int Nt, int SBN
 // The last (R mod ncu) tiles would leave most CUs idle in a final, ragged
 // round.  When they are at most half a round, each of them is cut along K into
 // S = ncu / tail slices (at most kMaxUnits slices in all, each at least NS
-// k-tiles deep): the slices form one full round and write fp32 partial tiles,
-// which ffn_gemm_fixup sums in slice order before the epilogue.
+// k-tiles deep): the slices form one full round and write fp32 partial rows,
+// which ffn_gemm_fixup sums in slice order before the epilogue.  Few tiles
+// (a few tokens per expert) are the same case: every tile is a tail tile, and
+// the partials cover only the tiles' real rows.
 constexpr int kMaxUnits = 256;
 
 struct TailPlan {
@@ -520,25 +522,31 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
     }
 }
 
-// fp32 partial tile of one K slice, lane-major so every access is a 16-byte
-// vector: [wave][i][j][r / 4][lane][r % 4] (r / 4 is the epilogue's column
-// group g), Cfg<BM>::UNIT floats per slice.
+// fp32 partial tile of one K slice, row-major [BM][BN] (Cfg<BM>::UNIT floats
+// per slice); only the tile's real rows are written (and later read), so a
+// slice of a tile with a few rows costs a few KB.  A lane holds columns
+// 8 g + 4 half + 0..3 of row l32 of each 32x32 MFMA tile (acc[i][j][4 g + q]).
 template <int BM>
 __device__ __forceinline__ void store_partial(const f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
-                                              float* __restrict__ dst) {
+                                              float* __restrict__ dst, int rows) {
     using G = Cfg<BM>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    f32x4_t* p = reinterpret_cast<f32x4_t*>(dst + (int64_t)wave * (G::UNIT / 4));
+    const int wn = wave % G::WN, wm = wave / G::WN;
+    const int l32 = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < G::FN; ++i)
+    for (int j = 0; j < G::FM; ++j) {
+        const int m = wm * G::TM + 32 * j + l32;
+        if (m >= rows) continue;
 #pragma unroll
-        for (int j = 0; j < G::FM; ++j)
+        for (int i = 0; i < G::FN; ++i)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4_t v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
-                                   acc[i][j][4 * r4 + 3]};
-                p[((i * G::FM + j) * 4 + r4) * 64 + lane] = v;
+            for (int g = 0; g < 4; ++g) {
+                const int n = wn * G::TN + 32 * i + 8 * g + 4 * half;
+                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                   acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4_t*>(dst + m * G::BN + n) = v;
             }
+    }
 }
 
 template <int BM>
@@ -622,18 +630,18 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     f32x16_t acc[G::FN][G::FM];
     zero_acc<BM>(acc);
     gemm_mainloop<BM>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
-    store_partial<BM>(acc, part + (int64_t)unit * G::UNIT);
+    store_partial<BM>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
 }
 
-// Tail tiles: workgroup (tile i, chunk c) takes 1024 of the tile's 16-byte
-// partial vectors, one per thread: the S slices summed in slice order, then
-// bias, activation, one rounding to bf16 and an 8-byte store.  A vector
-// [wave][i][j][g][lane] holds columns 8 g + 4 (lane / 32) + 0..3 of row
-// lane % 32 in MFMA tile (i, j) of that wave, as in the epilogue.
+// Tail tiles: workgroup (tile i, chunk c) takes rows 64 c .. 64 c + 63 of the
+// tile, 4 rows per pass (one per wave), 4 columns per lane: the S slices of
+// each 16-byte vector summed in slice order, then bias, activation, one
+// rounding to bf16 and an 8-byte store.  Rows past the tile's real rows were
+// never written and are not read.
 template <int BM>
 struct FixCfg {
-    static constexpr int VEC = Cfg<BM>::UNIT / 4;        // 16-byte vectors per tile
-    static constexpr int CHUNKS = VEC / 1024;            // workgroups per tile
+    static constexpr int ROWS = 64;                       // rows per workgroup
+    static constexpr int CHUNKS = BM / ROWS;              // workgroups per tile
 };
 
 template <int BM, int ACT>
@@ -650,38 +658,33 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     dense_coords(pl.full + i, pl.real_mt, Nt, SBN, mt, nt);
     TileRef tr;
     if (!tile_ref<BM>(offsets, E, mt, nt, tr)) return;
-    // vector index v within a slice: 4 such 1024-vector blocks per thread group
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int v = c * 1024 + it * 256 + (int)threadIdx.x;
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part) + (int64_t)i * pl.S * FixCfg<BM>::VEC + v;
-        f32x4_t a = src[0];
-        for (int s = 1; s < pl.S; ++s) {
-            const f32x4_t t = src[(int64_t)s * FixCfg<BM>::VEC];
+    const int rows = min(BM, tr.n_rows - tr.m0);
+    const int col = 4 * (threadIdx.x & 63);
+    if (tr.n0 + col >= N) return;                         // N % 4 == 0: all 4 columns valid
+    const int wave = threadIdx.x >> 6;
+    const float* src = part + (int64_t)i * pl.S * G::UNIT + col;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+        const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + (int64_t)tr.e * N + tr.n0 + col);
+        bv[0] = bf16_lo(bb[0]);
+        bv[1] = bf16_hi(bb[0]);
+        bv[2] = bf16_lo(bb[1]);
+        bv[3] = bf16_hi(bb[1]);
+    }
+    for (int r = c * FixCfg<BM>::ROWS + wave; r < min(rows, (c + 1) * FixCfg<BM>::ROWS); r += 4) {
+        const float* p = src + r * G::BN;
+        f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+        for (int sl = 1; sl < pl.S; ++sl) {
+            const f32x4_t t = *reinterpret_cast<const f32x4_t*>(p + (int64_t)sl * G::UNIT);
             a[0] += t[0]; a[1] += t[1]; a[2] += t[2]; a[3] += t[3];
         }
-        // decode [wave][i][j][g][lane]
-        const int lane = v & 63, g = (v >> 6) & 3, ij = (v >> 8) % (G::FN * G::FM);
-        const int wave = (v >> 8) / (G::FN * G::FM);
-        const int fi = ij / G::FM, fj = ij % G::FM;
-        const int wn = wave % G::WN, wm = wave / G::WN;
-        const int ml = wm * G::TM + 32 * fj + (lane & 31);
-        const int nl = wn * G::TN + 32 * fi + 8 * g + 4 * (lane >> 5);
-        if (tr.m0 + ml >= tr.n_rows || tr.n0 + nl >= N) continue;
-        float o[4] = {a[0], a[1], a[2], a[3]};
-        if (bias) {
-            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + (int64_t)tr.e * N + tr.n0 + nl);
-            o[0] += bf16_lo(bb[0]);
-            o[1] += bf16_hi(bb[0]);
-            o[2] += bf16_lo(bb[1]);
-            o[3] += bf16_hi(bb[1]);
-        }
+        float o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(o[q]);
+        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(a[q] + bv[q]);
         u32x2_t w;
         w[0] = pack_bf16x2(o[0], o[1]);
         w[1] = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<u32x2_t*>(C + (int64_t)(tr.row_begin + tr.m0 + ml) * N + tr.n0 + nl) = w;
+        *reinterpret_cast<u32x2_t*>(C + (int64_t)(tr.row_begin + tr.m0 + r) * N + tr.n0 + col) = w;
     }
 }
 
@@ -757,7 +760,10 @@ int pick_bm(const moe_problem_t& p) {
         cap = (int64_t)std::min<double>(c, (double)p.T);
     }
     const int64_t avg = std::min<int64_t>((p.T * p.k + p.E - 1) / p.E, cap);
-    if (avg <= 64) return 64;
+    // Few rows per expert: the GEMMs stream weights from HBM, and a row tile
+    // that holds a whole expert reads its weights once per column tile.  The
+    // 64-row layout only pays off below half a tile on average.
+    if (avg <= 32) return 64;
     if (avg <= 128) return 128;
     return 256;
 }
@@ -779,6 +785,21 @@ int device_cus() {
 
 int gemm_nt(int N) { return (N + 255) / 256; }
 
+// Every real tile, plus room for one round of K slices; the fixup covers at
+// most half a round of tail tiles (each is cut in 2 or more).
+template <int BM, int ACT>
+void launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
+                 int E, const uint16_t* w, const uint16_t* b, uint16_t* c, int K, int N, int Mt,
+                 int Nt, int SBN, int ncu, float* part, hipStream_t s) {
+    const int units = std::min(ncu, kMaxUnits);
+    const dim3 block(256);
+    ffn_gemm_bf16<BM, ACT><<<dim3((unsigned)((int64_t)Mt * Nt + units)), block, 0, s>>>(
+        x, xb, rowmap, offsets, E, w, b, c, K, N, Nt, SBN, ncu, part);
+    if (part)
+        ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
+            offsets, E, b, c, K, N, Nt, SBN, ncu, part);
+}
+
 template <int ACT>
 hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* rowmap,
                        const int32_t* offsets, const void* W, const void* bias, void* Cout,
@@ -791,9 +812,6 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         // super-block width in column tiles: the widest of 16/8/4 that divides Nt
         const int SBN = (Nt % 16 == 0) ? 16 : (Nt % 8 == 0) ? 8 : 4;
         const int ncu = device_cus();
-        const int units = std::min(ncu, kMaxUnits);
-        // every real tile, plus room for one round of K slices
-        const dim3 grid((unsigned)((int64_t)Mt * Nt + units)), block(256);
         auto* x = static_cast<const uint16_t*>(X);
         auto* w = static_cast<const uint16_t*>(W);
         auto* b = static_cast<const uint16_t*>(bias);
@@ -801,26 +819,12 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         // bytes addressable through X: the token rows (gather) or the kept rows
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
-        // tail tiles are at most units / 2 (every tail tile is cut in 2 or more)
-        if (bm == 256) {
-            ffn_gemm_bf16<256, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
-                                                          K, N, Nt, SBN, ncu, part);
-            if (part)
-                ffn_gemm_fixup<256, ACT><<<dim3((unsigned)(units / 2 * FixCfg<256>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
-                                                                SBN, ncu, part);
-        } else if (bm == 128) {
-            ffn_gemm_bf16<128, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
-                                                          K, N, Nt, SBN, ncu, part);
-            if (part)
-                ffn_gemm_fixup<128, ACT><<<dim3((unsigned)(units / 2 * FixCfg<128>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
-                                                                SBN, ncu, part);
-        } else {
-            ffn_gemm_bf16<64, ACT><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, p.E, w, b, c,
-                                                         K, N, Nt, SBN, ncu, part);
-            if (part)
-                ffn_gemm_fixup<64, ACT><<<dim3((unsigned)(units / 2 * FixCfg<64>::CHUNKS)), block, 0, s>>>(offsets, p.E, b, c, K, N, Nt,
-                                                               SBN, ncu, part);
-        }
+        if (bm == 256)
+            launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
+        else if (bm == 128)
+            launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
+        else
+            launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
         const int Nt = (N + 63) / 64;

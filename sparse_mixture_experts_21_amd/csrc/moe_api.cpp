@@ -83,7 +83,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
         if ((int64_t)p->H * p->F * 2 >= lim) return MOE_ERR_UNSUPPORTED;
         if ((int64_t)p->E * p->H * 2 >= lim) return MOE_ERR_UNSUPPORTED;
         const int64_t tiles = (p->T * p->k / 64 + p->E + 1) * (((int64_t)std::max(p->H, p->F) + 255) / 256);
-        if (tiles + 256 >= lim) return MOE_ERR_UNSUPPORTED;
+        if (tiles + 256 >= lim) return MOE_ERR_UNSUPPORTED;   // + a round of K slices
     }
     return MOE_OK;
 }

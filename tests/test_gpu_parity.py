@@ -232,13 +232,18 @@ def _tail_plan_host(offsets, bm, nt, ncu, nk, ns=4, max_units=256):
 SPLIT = S("split_T4096_H512_E8_k2_F2048", 4096, 512, 8, 2, 2048)
 
 
-@pytest.mark.parametrize("act", ["gelu", "silu"])
-def test_expert_ffn_tail_split(act):
+# few rows per expert (64-row tiles): every tile of both GEMMs is cut along K
+SPLIT_SMALL = S("split_small_T4_H512_E8_k2_F2048", 4, 512, 8, 2, 2048, biases=True)
+
+
+@pytest.mark.parametrize("spec", [SPLIT, SPLIT.replace(act="silu", name=SPLIT.name + "_silu"),
+                                  SPLIT_SMALL], ids=lambda s: s.name)
+def test_expert_ffn_tail_split(spec):
     """With a workspace, the last round of tiles is cut along K (fp32 partials
     summed in slice order); the result must match the oracle like whole tiles
-    do.  At this shape the up GEMM cuts 40 of ~296 tiles and the down GEMM
-    cuts all of its ~74 tiles (no whole tile at all)."""
-    spec = SPLIT.replace(act=act, name=f"{SPLIT.name}_{act}")
+    do.  At the T=4096 shape the up GEMM cuts 40 of ~296 tiles and the down
+    GEMM cuts all of its ~74 tiles (no whole tile at all); at T=4 every tile of
+    both GEMMs is cut, with one or two real rows per tile."""
     say(f"[expert_ffn tail split] {spec.name}")
     inp = W.generate(spec)
     ref = om.route(spec, om.logits(spec, inp["x"], inp["Wg"], inp["bg"]))
@@ -246,8 +251,10 @@ def test_expert_ffn_tail_split(act):
     off_h = dsp["offsets"]
     A = int(off_h[-1])
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    up = _tail_plan_host(off_h, 256, (spec.F + 255) // 256, ncu, spec.H // 32)
-    down = _tail_plan_host(off_h, 256, (spec.H + 255) // 256, ncu, spec.F // 32)
+    avg = -(-spec.T * spec.k // spec.E)
+    bm = 64 if avg <= 32 else 128 if avg <= 128 else 256
+    up = _tail_plan_host(off_h, bm, (spec.F + 255) // 256, ncu, spec.H // 32)
+    down = _tail_plan_host(off_h, bm, (spec.H + 255) // 256, ncu, spec.F // 32)
     say(f"    tail plan on {ncu} CUs: up {up}, down {down}")
     assert up[1] >= 2 and down[1] >= 2, "shape no longer exercises the K split"
     rows = inp["x"][dsp["row_token"][:A]]
@@ -304,7 +311,7 @@ def _sample_tokens(spec, pos, n=48, seed=0):
     return np.array(sorted(pick), dtype=np.int64)
 
 
-FULL = ["c2", "c3", "c4", "c5", "c5s"]
+FULL = ["c2", "c3", "c4", "c5", "c5s", "d1", "d8", "d64", "d256"]
 
 
 @pytest.mark.parametrize("name", FULL + ["c2_cf1.0"])

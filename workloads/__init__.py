@@ -100,6 +100,14 @@ CONFIGS: Dict[str, Spec] = {
     "c5s": Spec("mixtral_silu_T16384_H4096_E8_k2_F14336_dropless", T=16384, H=4096, E=8,
                 k=2, F=14336, dtype="bf16", cf=0.0, seed=6, act="silu"),
 }
+# Decode-shaped forwards of the Mixtral-shaped layer (the pages' inference
+# setting: a few tokens, only their top-k experts active, no capacity limit).
+# Every T shares the seed, so the weights are identical and x of a smaller T is
+# the leading rows of x of a larger one (draws are in C order).
+for _t in (1, 8, 64, 256):
+    CONFIGS[f"d{_t}"] = Spec(f"mixtral_decode_T{_t}_H4096_E8_k2_F14336_dropless", T=_t, H=4096,
+                             E=8, k=2, F=14336, dtype="bf16", cf=0.0, seed=8)
+del _t
 
 
 # ----------------------------------------------------------------------------
