@@ -251,7 +251,8 @@ struct TileRef {
 // slots per 16 lanes; the DMA writes are 1 KB contiguous per instruction.
 // DMA pipeline and MFMA loop over the k-tiles [kb, kb + nkr) of tile `tr`,
 // accumulating into acc (the caller zeroes it).  `lds` holds Cfg<BM>::LDS_BYTES.
-template <int BM>
+// NTW: weight loads carry the nontemporal hint (see ffn_gemm_bf16).
+template <int BM, bool NTW>
 __device__ __forceinline__ void gemm_mainloop(
     const TileRef& tr, int kb, int nkr, char* lds, const uint16_t* __restrict__ X,
     uint32_t x_bytes, const int32_t* __restrict__ rowmap, const uint16_t* __restrict__ W, int K,
@@ -300,8 +301,10 @@ __device__ __forceinline__ void gemm_mainloop(
         const uint32_t st = lds0 + (uint32_t)((t % G::NS) * G::STAGE);
         const int k0 = (kb + t) * G::BK;
         if (q < G::WI) {
-            dma16(w_rsrc, woff[q] + (uint32_t)(kb + t) * wstep,
-                  __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024)));
+            const uint32_t o = woff[q] + (uint32_t)(kb + t) * wstep;
+            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024));
+            if constexpr (NTW) dma16_nt(w_rsrc, o, l);
+            else dma16(w_rsrc, o, l);
         } else {
             const int qx = q - G::WI;
             const uint32_t o = (k0 + xk[qx] < K) ? xoff[qx] + (uint32_t)k0 * 2u : kOob;
@@ -567,7 +570,7 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
 }
 
 // One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
-template <int TB, int ACT>
+template <int TB, int ACT, bool NTW>
 __device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
                                            const uint16_t* __restrict__ X, uint32_t x_bytes,
                                            const int32_t* __restrict__ rowmap,
@@ -576,7 +579,7 @@ __device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
                                            uint16_t* __restrict__ C, int K, int N) {
     f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
     zero_acc<TB>(acc);
-    gemm_mainloop<TB>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_mainloop<TB, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
     gemm_epilogue<TB, ACT>(tr, acc, lds, bias, C, N);
 }
 
@@ -593,6 +596,11 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     int ncu, float* __restrict__ part) {
     using G = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
+    // With at most 128 rows per tile (few rows per expert) an expert's weights
+    // are read about once, so they stream past the last-level cache instead of
+    // evicting (and writing back) other kernels' lines; the 256-row layout
+    // re-reads weight tiles across row tiles and keeps the default policy.
+    constexpr bool kNtW = BM <= 128;
     const int nk = (K + G::BK - 1) / G::BK;
     const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, part != nullptr);
     const int p = blockIdx.x;
@@ -614,22 +622,22 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         const int rows = tr.n_rows - tr.m0;
         if constexpr (BM >= 128) {
             if (rows <= 64) {
-                whole_tile<64, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                whole_tile<64, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
                 return;
             }
         }
         if constexpr (BM >= 256) {
             if (rows <= 128) {
-                whole_tile<128, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                whole_tile<128, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
                 return;
             }
         }
-        whole_tile<BM, ACT>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+        whole_tile<BM, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
         return;
     }
     f32x16_t acc[G::FN][G::FM];
     zero_acc<BM>(acc);
-    gemm_mainloop<BM>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_mainloop<BM, kNtW>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
     store_partial<BM>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
 }
 
