@@ -329,13 +329,13 @@ def main():
     if not args.no_abi_timing:
         log("[bench] timing each ABI call alone (warm and cold)")
         abi, A_abi = stage_timing(moe, torch, spec, prob, d, log)
-    stage = np.array([ev.stage_ms() for ev in evs])          # [steps][5]
+    stage = np.array([ev.stage_ms() for ev in evs])          # [steps][stages]
     stage_mean = stage.mean(axis=0)
     A = int(offsets[-1].item())
     names = moe.STAGE_NAMES
     sm = {n: float(v) for n, v in zip(names, stage_mean)}
     gemm_flops = 2.0 * A * H * F                              # per GEMM launch
-    ffn_ms = sm["ffn_up"] + sm["ffn_down"]
+    ffn_ms = sm["ffn_up"] + sm["ffn_up_fixup"] + sm["ffn_down"] + sm["ffn_down_fixup"]
     ffn_tflops = 2 * gemm_flops / (ffn_ms * 1e-3) / 1e12
     dom = "ffn_up" if sm["ffn_up"] >= sm["ffn_down"] else "ffn_down"
     s = spec.elem_bytes

@@ -84,15 +84,20 @@ typedef struct {
 
 /* Events recorded by moe_forward when `stage_events` is non-NULL: event i is
  * recorded on `stream` just before stage i starts, the last one after the
- * final stage.  The FFN up and down stages are one kernel launch each. */
+ * final stage.  MOE_EV_FFN_UP and MOE_EV_FFN_DOWN start the two expert GEMM
+ * launches alone; the *_FIXUP stages that follow each sum the K slices of the
+ * tiles cut in its last round and apply the epilogue to them (empty when no
+ * tile is cut). */
 enum {
     MOE_EV_ROUTE = 0,
     MOE_EV_PERMUTE = 1,
     MOE_EV_FFN_UP = 2,
-    MOE_EV_FFN_DOWN = 3,
-    MOE_EV_COMBINE = 4,
-    MOE_EV_END = 5,
-    MOE_FORWARD_EVENTS = 6
+    MOE_EV_FFN_UP_FIXUP = 3,
+    MOE_EV_FFN_DOWN = 4,
+    MOE_EV_FFN_DOWN_FIXUP = 5,
+    MOE_EV_COMBINE = 6,
+    MOE_EV_END = 7,
+    MOE_FORWARD_EVENTS = 8
 };
 
 /* Expert capacity (host, synchronous): T when capacity_factor <= 0, else

@@ -24,9 +24,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
 MOE_ROUTE_LOGITS_IN = 1
-(MOE_EV_ROUTE, MOE_EV_PERMUTE, MOE_EV_FFN_UP, MOE_EV_FFN_DOWN, MOE_EV_COMBINE,
- MOE_EV_END, MOE_FORWARD_EVENTS) = range(7)
-STAGE_NAMES = ("route", "permute", "ffn_up", "ffn_down", "combine")
+(MOE_EV_ROUTE, MOE_EV_PERMUTE, MOE_EV_FFN_UP, MOE_EV_FFN_UP_FIXUP, MOE_EV_FFN_DOWN,
+ MOE_EV_FFN_DOWN_FIXUP, MOE_EV_COMBINE, MOE_EV_END, MOE_FORWARD_EVENTS) = range(9)
+STAGE_NAMES = ("route", "permute", "ffn_up", "ffn_up_fixup", "ffn_down", "ffn_down_fixup",
+               "combine")
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string")

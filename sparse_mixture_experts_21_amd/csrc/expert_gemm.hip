@@ -641,15 +641,16 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     store_partial<BM>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
 }
 
-// Tail tiles: workgroup (tile i, chunk c) takes rows 64 c .. 64 c + 63 of the
+// Tail tiles: workgroup (tile i, chunk c) takes rows 16 c .. 16 c + 15 of the
 // tile, 4 rows per pass (one per wave), 4 columns per lane: the S slices of
-// each 16-byte vector summed in slice order, then bias, activation, one
-// rounding to bf16 and an 8-byte store.  Rows past the tile's real rows were
-// never written and are not read.
+// each 16-byte vector loaded 8 at a time and summed in slice order, then bias,
+// activation, one rounding to bf16 and an 8-byte store.  Rows past the tile's
+// real rows were never written and are not read.
 template <int BM>
 struct FixCfg {
-    static constexpr int ROWS = 64;                       // rows per workgroup
+    static constexpr int ROWS = 16;                       // rows per workgroup
     static constexpr int CHUNKS = BM / ROWS;              // workgroups per tile
+    static constexpr int BATCH = 8;                       // slice loads in flight
 };
 
 template <int BM, int ACT>
@@ -682,9 +683,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     for (int r = c * FixCfg<BM>::ROWS + wave; r < min(rows, (c + 1) * FixCfg<BM>::ROWS); r += 4) {
         const float* p = src + r * G::BN;
         f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-        for (int sl = 1; sl < pl.S; ++sl) {
-            const f32x4_t t = *reinterpret_cast<const f32x4_t*>(p + (int64_t)sl * G::UNIT);
-            a[0] += t[0]; a[1] += t[1]; a[2] += t[2]; a[3] += t[3];
+        for (int s0 = 1; s0 < pl.S; s0 += FixCfg<BM>::BATCH) {
+            // unconditional loads at clamped slice indices, masked in the sum
+            f32x4_t t[FixCfg<BM>::BATCH];
+#pragma unroll
+            for (int u = 0; u < FixCfg<BM>::BATCH; ++u)
+                t[u] = *reinterpret_cast<const f32x4_t*>(
+                    p + (int64_t)min(s0 + u, pl.S - 1) * G::UNIT);
+#pragma unroll
+            for (int u = 0; u < FixCfg<BM>::BATCH; ++u) {
+                if (s0 + u < pl.S) {
+                    a[0] += t[u][0]; a[1] += t[u][1]; a[2] += t[u][2]; a[3] += t[u][3];
+                }
+            }
         }
         float o[4];
 #pragma unroll
@@ -796,22 +807,26 @@ int gemm_nt(int N) { return (N + 255) / 256; }
 // Every real tile, plus room for one round of K slices; the fixup covers at
 // most half a round of tail tiles (each is cut in 2 or more).
 template <int BM, int ACT>
-void launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
+hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
                  int E, const uint16_t* w, const uint16_t* b, uint16_t* c, int K, int N, int Mt,
-                 int Nt, int SBN, int ncu, float* part, hipStream_t s) {
+                 int Nt, int SBN, int ncu, float* part, hipEvent_t mid, hipStream_t s) {
     const int units = std::min(ncu, kMaxUnits);
     const dim3 block(256);
     ffn_gemm_bf16<BM, ACT><<<dim3((unsigned)((int64_t)Mt * Nt + units)), block, 0, s>>>(
         x, xb, rowmap, offsets, E, w, b, c, K, N, Nt, SBN, ncu, part);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
+    if (e != hipSuccess) return e;
     if (part)
         ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
             offsets, E, b, c, K, N, Nt, SBN, ncu, part);
+    return hipGetLastError();
 }
 
 template <int ACT>
 hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* rowmap,
                        const int32_t* offsets, const void* W, const void* bias, void* Cout,
-                       int K, int N, float* part, hipStream_t s) {
+                       int K, int N, float* part, hipEvent_t mid, hipStream_t s) {
     const int64_t rows = p.T * p.k;
     if (p.dtype == MOE_DTYPE_BF16) {
         const int bm = pick_bm(p);
@@ -827,35 +842,42 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         // bytes addressable through X: the token rows (gather) or the kept rows
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
+        hipError_t e;
         if (bm == 256)
-            launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
+            e = launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+                                  mid, s);
         else if (bm == 128)
-            launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
+            e = launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+                                  mid, s);
         else
-            launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part, s);
+            e = launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+                                 mid, s);
+        return e;
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
         const int Nt = (N + 63) / 64;
         ffn_gemm_f32<ACT><<<dim3((unsigned)((int64_t)Mt * Nt)), dim3(256), 0, s>>>(
             static_cast<const float*>(X), rowmap, offsets, p.E, static_cast<const float*>(W),
             static_cast<const float*>(bias), static_cast<float*>(Cout), K, N, Mt);
+        const hipError_t e = hipGetLastError();
+        return (e == hipSuccess && mid) ? hipEventRecord(mid, s) : e;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         float* part, hipStream_t s) {
+                         float* part, hipEvent_t mid, hipStream_t s) {
     if (p.activation == MOE_ACT_SILU)
-        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, s);
-    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, s);
+        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, mid, s);
+    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, mid, s);
 }
 
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
-                           const void* W2, const void* b2, void* y, float* part, hipStream_t s) {
-    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, p.F, p.H, part, s);
+                           const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
+                           hipStream_t s) {
+    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, p.F, p.H, part, mid, s);
 }
 
 size_t gemm_partial_bytes(const moe_problem_t& p) {

@@ -176,8 +176,8 @@ moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_
     // is cut along K (see moe_workspace_bytes)
     float* part = (ws && aligned16(ws) && ws_bytes >= gemm_partial_bytes(*p))
                       ? static_cast<float*>(ws) : nullptr;
-    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, part, stream);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, part, stream);
+    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, part, nullptr, stream);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, part, nullptr, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -235,9 +235,11 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
                            stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
     float* part = reinterpret_cast<float*>(w + L.gemm_part);
-    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, part, stream);
+    hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
+    hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
+    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, part, up_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, stream);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
     if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
     if (e == hipSuccess) e = ev(MOE_EV_END);

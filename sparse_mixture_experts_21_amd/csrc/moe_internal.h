@@ -78,11 +78,13 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
 // instead of xp[r] (the gather fused into the operand load).
 // part (nullable): fp32 buffer of gemm_partial_bytes(p) for the K slices of
 // the ragged last round of tiles; without it no tile is cut.
+// mid (nullable): event recorded between the GEMM launch and its fixup.
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         float* part, hipStream_t s);
+                         float* part, hipEvent_t mid, hipStream_t s);
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
-                           const void* W2, const void* b2, void* y, float* part, hipStream_t s);
+                           const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
+                           hipStream_t s);
 size_t gemm_partial_bytes(const moe_problem_t& p);
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s);
