@@ -51,6 +51,9 @@ def lib():
         L.orc_forward_tokens.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          ctypes.c_int64, vp]
         L.orc_combine.argtypes = [P, vp, vp, vp, vp]
+        L.orc_expert_choice.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp]
+        L.orc_ec_capacity.argtypes = [P, ctypes.c_int64]
+        L.orc_ec_capacity.restype = ctypes.c_int64
         L.orc_num_threads.argtypes = []
         _lib = L
     return _lib
@@ -188,6 +191,57 @@ def forward(spec, inp: Dict[str, Optional[np.ndarray]], tokens: Optional[Sequenc
     res: Dict[str, object] = dict(logits=lg, cap=capacity(spec), out=out, tokens=toks)
     res.update(r)
     res.update(dsp)
+    return res
+
+
+# ---------------------------------------------------------------- expert choice
+def ec_capacity(spec, group: int) -> int:
+    return int(lib().orc_ec_capacity(ctypes.byref(problem(spec)), int(group)))
+
+
+def expert_choice(spec, lg: np.ndarray, group: int) -> Dict[str, np.ndarray]:
+    """Expert-choice routing on logits [T][E]: per group of `group` tokens each
+    expert takes its C tokens with the largest logits.  Returns sel
+    [E][T/group][C] (ascending tokens), rowof [T][E] (expert-major row of each
+    taken (token, expert), -1 when not taken), probs [T][E] (softmax weights),
+    offsets [E+1] (every expert holds (T/group) * C rows) and C."""
+    T, E = spec.T, spec.E
+    C = ec_capacity(spec, group)
+    ng = T // group
+    sel = np.empty((E, ng, C), np.int32)
+    rowof = np.empty((T, E), np.int32)
+    probs = np.empty((T, E), np.float64)
+    _check(lib().orc_expert_choice(ctypes.byref(problem(spec)), int(group),
+                                   _ptr(np.ascontiguousarray(lg, np.float64)), _ptr(sel),
+                                   _ptr(rowof), _ptr(probs)), "expert_choice")
+    offsets = (np.arange(E + 1, dtype=np.int64) * ng * C).astype(np.int32)
+    return dict(sel=sel, rowof=rowof, probs=probs, offsets=offsets, C=C)
+
+
+def ec_forward_tokens(spec, x, rowof, probs, W1, b1, W2, b2,
+                      tokens: Sequence[int]) -> np.ndarray:
+    """Expert-choice layer output of the listed tokens: the sum, over the
+    experts that took the token in expert order, of its softmax weight times
+    the expert's output.  The same per-token loop as forward_tokens, with one
+    slot per expert (slot e is expert e, kept when rowof[t][e] >= 0)."""
+    T, E = spec.T, spec.E
+    slots = np.broadcast_to(np.arange(E, dtype=np.int32), (T, E))
+    return forward_tokens(spec.replace(k=E), x, slots, probs, rowof, W1, b1, W2, b2, tokens)
+
+
+def ec_forward(spec, inp: Dict[str, Optional[np.ndarray]], group: int,
+               tokens: Optional[Sequence[int]] = None,
+               given_logits: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """The expert-choice layer: logits -> expert choice -> expert FFN and
+    combine, for all tokens or the listed ones."""
+    lg = logits(spec, inp["x"], inp["Wg"], inp.get("bg")) if given_logits is None \
+        else np.ascontiguousarray(given_logits, np.float64)
+    r = expert_choice(spec, lg, group)
+    toks = np.arange(spec.T) if tokens is None else np.asarray(tokens, np.int64)
+    out = ec_forward_tokens(spec, inp["x"], r["rowof"], r["probs"], inp["W1"], inp.get("b1"),
+                            inp["W2"], inp.get("b2"), toks)
+    res: Dict[str, object] = dict(logits=lg, out=out, tokens=toks)
+    res.update(r)
     return res
 
 

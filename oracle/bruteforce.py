@@ -22,7 +22,12 @@ mismatch:
   the (token, slot) pairs and ``index_add_`` back into token rows (no
   capacity limit).
 
-All three follow ``spec.act``: ``nn.GELU`` (exact erf) as in the reference
+* ``expert_choice_dense`` / ``torch_expert_choice_sets`` — expert-choice
+  routing (Core Concepts, 2. Routing Mechanisms) by a stable lexicographic sort
+  per (expert, group) with every expert evaluated densely, and by the page's
+  own ``torch.topk`` over the sequence axis.
+
+All of them follow ``spec.act``: ``nn.GELU`` (exact erf) as in the reference
 layer, or ``nn.SiLU`` as in the Mixtral block; the numpy route evaluates SiLU
 as ``a * expit(a)`` and GELU with ``scipy.special.erf``.
 """
@@ -44,6 +49,19 @@ def _capacity(spec) -> int:
     if not spec.cf > 0:
         return spec.T
     return int(np.ceil(spec.cf * spec.T * spec.k / spec.E))
+
+
+def _all_experts(spec, x, W1, b1, W2, b2) -> np.ndarray:
+    """Every expert on every token, [E][T][H], with dense matrix products."""
+    Y = np.empty((spec.E, x.shape[0], spec.H))
+    for e in range(spec.E):
+        a = x @ W1[e] + (0.0 if b1 is None else b1[e][None, :])
+        if spec.act == "silu":
+            g = a * special.expit(a)
+        else:
+            g = 0.5 * a * (1.0 + special.erf(a / np.sqrt(2.0)))
+        Y[e] = g @ W2[e] + (0.0 if b2 is None else b2[e][None, :])
+    return Y
 
 
 def dense_then_mask(spec, inp: Dict[str, Optional[np.ndarray]]) -> Dict[str, object]:
@@ -77,15 +95,7 @@ def dense_then_mask(spec, inp: Dict[str, Optional[np.ndarray]]) -> Dict[str, obj
     offsets = np.concatenate([[0], np.cumsum(kept_per_e)]).astype(np.int32)
     pos = np.where(kept, offsets[idx.ravel()] + rank, -1).reshape(T, k).astype(np.int32)
 
-    # every expert on every token
-    Y = np.empty((E, T, H))
-    for e in range(E):
-        a = x @ W1[e] + (0.0 if b1 is None else b1[e][None, :])
-        if spec.act == "silu":
-            g = a * special.expit(a)
-        else:
-            g = 0.5 * a * (1.0 + special.erf(a / np.sqrt(2.0)))
-        Y[e] = g @ W2[e] + (0.0 if b2 is None else b2[e][None, :])
+    Y = _all_experts(spec, x, W1, b1, W2, b2)
     sel = Y[idx, np.arange(T)[:, None], :]           # [T, k, H]
     coef = w * kept.reshape(T, k)
     out = np.einsum("tk,tkh->th", coef, sel)
@@ -180,3 +190,47 @@ def dense_ffn(spec, inp, e: int = 0) -> np.ndarray:
     x = torch.from_numpy(_f64(inp["x"], spec.dtype))
     with torch.no_grad():
         return experts[e](x).numpy()
+
+
+# ---------------------------------------------------------------- expert choice
+def expert_choice_dense(spec, inp: Dict[str, Optional[np.ndarray]], group: int,
+                        C: int) -> Dict[str, object]:
+    """Expert-choice routing by sorting: in every group each expert's tokens are
+    ordered by (descending logit, ascending token) with a stable lexicographic
+    sort and the first C are taken; then every expert runs on every token and
+    the taken outputs are summed with the tokens' softmax weights (a 0/1 mask
+    per (token, expert))."""
+    d = spec.dtype
+    T, E = spec.T, spec.E
+    x = _f64(inp["x"], d)
+    Wg, bg = _f64(inp["Wg"], d), _f64(inp.get("bg"), d)
+    lg = x @ Wg + (0.0 if bg is None else bg[None, :])
+    p = special.softmax(lg, axis=1)
+    ng = T // group
+    mask = np.zeros((T, E), bool)
+    sets = np.empty((E, ng, C), np.int64)
+    for e in range(E):
+        for g in range(ng):
+            toks = np.arange(g * group, (g + 1) * group)
+            order = np.lexsort((toks, -lg[toks, e]))    # last key is primary
+            take = np.sort(toks[order[:C]])
+            sets[e, g] = take
+            mask[take, e] = True
+    Y = _all_experts(spec, x, _f64(inp["W1"], d), _f64(inp.get("b1"), d), _f64(inp["W2"], d),
+                     _f64(inp.get("b2"), d))
+    out = np.einsum("te,eth->th", p * mask, Y)
+    return dict(logits=lg, probs=p, mask=mask, sets=sets, out=out, Y=Y)
+
+
+def torch_expert_choice_sets(lg: np.ndarray, group: int, C: int) -> np.ndarray:
+    """The page's expert-choice snippet (Core Concepts, 2. Routing Mechanisms):
+    scores laid out (batch, experts, seq_len), torch.topk over the sequence.
+    Returns the taken tokens [E][groups][C], ascending (torch.topk leaves the
+    order of equal scores open, so callers use inputs without ties)."""
+    import torch
+    T, E = lg.shape
+    ng = T // group
+    scores = torch.from_numpy(lg).reshape(ng, group, E).transpose(-1, -2)   # (ng, E, group)
+    idx = torch.topk(scores, k=C, dim=-1).indices                         # (ng, E, C)
+    glob = idx + (torch.arange(ng) * group)[:, None, None]
+    return np.sort(glob.permute(1, 0, 2).numpy(), axis=-1)

@@ -321,3 +321,70 @@ int orc_combine(const orc_problem* p, const void* y, const int32_t* pos,
     }
     return 0;
 }
+
+int64_t orc_ec_capacity(const orc_problem* p, int64_t group) {
+    const double cf = p->cf > 0.0 ? p->cf : 1.0;
+    double c = ceil(cf * (double)group * (double)p->k / (double)p->E);
+    if (c < 1.0) c = 1.0;
+    if (c > (double)group) c = (double)group;
+    return (int64_t)c;
+}
+
+int orc_expert_choice(const orc_problem* p, int64_t group, const double* logits,
+                      int32_t* sel, int32_t* rowof, double* probs) {
+    if (!valid(p) || group < 1 || p->T % group != 0 || !logits || !sel || !rowof || !probs)
+        return -1;
+    const int64_t T = p->T, G = group, ng = T / group;
+    const int E = p->E;
+    const int64_t C = orc_ec_capacity(p, group);
+
+    /* each token's softmax over the experts, shifted by its maximum logit */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* l = logits + t * E;
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m) m = l[e];
+        double Z = 0.0;
+        for (int e = 0; e < E; ++e) Z += exp(l[e] - m);
+        for (int e = 0; e < E; ++e) {
+            probs[t * E + e] = exp(l[e] - m) / Z;
+            rowof[t * E + e] = -1;
+        }
+    }
+
+    /* each (expert, group): C passes of "first maximum" over the untaken
+     * tokens of the group, then the taken tokens listed in token order */
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < (int64_t)E * ng; ++q) {
+        const int e = (int)(q / ng);
+        const int64_t g = q % ng;
+        char* taken = (char*)calloc((size_t)G, 1);
+        if (!taken) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int64_t s = 0; s < C; ++s) {
+            int64_t best = -1;
+            for (int64_t i = 0; i < G; ++i) {
+                if (taken[i]) continue;
+                if (best < 0 || logits[(g * G + i) * E + e] > logits[(g * G + best) * E + e])
+                    best = i;
+            }
+            taken[best] = 1;
+        }
+        int64_t j = 0;
+        for (int64_t i = 0; i < G; ++i) {
+            if (!taken[i]) continue;
+            const int64_t t = g * G + i;
+            const int64_t row = (e * ng + g) * C + j;
+            sel[row] = (int32_t)t;
+            rowof[t * E + e] = (int32_t)row;
+            ++j;
+        }
+        free(taken);
+    }
+    return bad ? -2 : 0;
+}

@@ -77,6 +77,25 @@ int orc_forward_tokens(const orc_problem* p, const void* x, const int32_t* topk_
 int orc_combine(const orc_problem* p, const void* y, const int32_t* pos,
                 const double* topk_w, double* out);
 
+/* Expert-choice routing ("moe-training" SKILL page, Core Concepts, 2. Routing
+ * Mechanisms: expert choice; experts pick tokens instead of tokens picking
+ * experts).  The T tokens form T / group groups of `group` consecutive tokens
+ * (a sequence each); in every group each expert takes C = orc_ec_capacity
+ * tokens: those with the largest logits[t][e], taken one at a time as the
+ * first maximum over the untaken tokens (descending value, equal values lower
+ * token first).  Outputs:
+ *   sel   [E][T/group][C]  taken tokens of each (expert, group), ascending;
+ *   rowof [T][E]           row (e * (T/group) + g) * C + j of token
+ *                          sel[e][g][j] in the expert-major row order, else -1;
+ *   probs [T][E]           softmax of each token's logits over the experts:
+ *                          its weight for each expert that takes it. */
+int orc_expert_choice(const orc_problem* p, int64_t group, const double* logits,
+                      int32_t* sel, int32_t* rowof, double* probs);
+
+/* Expert-choice capacity: ceil(cf * group * k / E) in double, with cf <= 0
+ * read as 1 (each expert takes its balanced share), clamped to [1, group]. */
+int64_t orc_ec_capacity(const orc_problem* p, int64_t group);
+
 /* Number of OpenMP threads the oracle uses. */
 int orc_num_threads(void);
 

@@ -300,3 +300,103 @@ def test_dispatch_invariants_ds_shaped_routing(oracle_mod):
     o["cap"] = oracle_mod.capacity(spec)
     assert o["cap"] == 2048
     check_dispatch_invariants(spec, o)
+
+
+# ---------------------------------------------------------------- expert choice
+EC_CASES = [
+    dict(T=24, E=4, k=1, group=24),
+    dict(T=24, E=4, k=2, group=8),
+    dict(T=30, E=3, k=1, cf=1.5, group=10),
+    dict(T=16, E=8, k=2, cf=0.25, group=16, dtype="bf16"),
+    dict(T=20, E=5, k=3, group=5, act="silu"),
+    dict(T=12, E=2, k=1, cf=4.0, group=6, biases=False),   # C = group: every token
+]
+
+
+def _ec(case):
+    case = dict(case)
+    group = case.pop("group")
+    return tiny(**case), group
+
+
+@pytest.mark.parametrize("case", EC_CASES, ids=[str(c) for c in EC_CASES])
+def test_expert_choice_matches_sorting_and_dense_experts(oracle_mod, case):
+    spec, group = _ec(case)
+    inp = W.generate(spec, workers=1)
+    o = oracle_mod.ec_forward(spec, inp, group)
+    C = o["C"]
+    b = bf.expert_choice_dense(spec, inp, group, C)
+    np.testing.assert_allclose(o["logits"], b["logits"], rtol=RT, atol=AT)
+    assert np.array_equal(o["sel"], b["sets"])
+    assert np.array_equal(o["rowof"] >= 0, b["mask"])
+    np.testing.assert_allclose(o["probs"], b["probs"], rtol=RT, atol=AT)
+    np.testing.assert_allclose(o["out"], b["out"], rtol=RT, atol=1e-11)
+
+
+@pytest.mark.parametrize("case", EC_CASES[:5], ids=[str(c) for c in EC_CASES[:5]])
+def test_expert_choice_matches_torch_topk_snippet(oracle_mod, case):
+    spec, group = _ec(case)
+    inp = W.generate(spec, workers=1)
+    lg = oracle_mod.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    r = oracle_mod.expert_choice(spec, lg, group)
+    assert np.array_equal(r["sel"], bf.torch_expert_choice_sets(lg, group, r["C"]))
+
+
+def test_expert_choice_structure(oracle_mod):
+    spec, group = _ec(dict(T=48, E=6, k=2, cf=1.25, group=12))
+    inp = W.generate(spec, workers=1)
+    lg = oracle_mod.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    r = oracle_mod.expert_choice(spec, lg, group)
+    E, T, C, ng = spec.E, spec.T, r["C"], spec.T // group
+    assert C == math.ceil(1.25 * group * 2 / E) == 5
+    # perfect balance: every expert holds exactly ng * C rows
+    assert np.array_equal(np.diff(r["offsets"]), np.full(E, ng * C))
+    rows = r["rowof"][r["rowof"] >= 0]
+    assert np.array_equal(np.sort(rows), np.arange(E * ng * C))     # a bijection onto the rows
+    for e in range(E):
+        for g in range(ng):
+            take = r["sel"][e, g]
+            assert np.all(np.diff(take) > 0) and np.all(take // group == g)
+            for j, t in enumerate(take):
+                assert r["rowof"][t, e] == (e * ng + g) * C + j
+            rest = np.setdiff1d(np.arange(g * group, (g + 1) * group), take)
+            assert lg[take, e].min() > lg[rest, e].max()              # no ties in this draw
+    np.testing.assert_allclose(r["probs"].sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_expert_choice_ties_take_lower_tokens(oracle_mod):
+    """All-zero gate: every logit ties, so each expert takes the first C
+    tokens of every group; with identical experts the output is the dense FFN
+    on those tokens (weight E * 1/E) and zero elsewhere."""
+    spec = W.zero_gate(tiny(T=20, E=4, k=1, identical_experts=True))
+    group = 10
+    inp = W.generate(spec, workers=1)
+    o = oracle_mod.ec_forward(spec, inp, group)
+    C = o["C"]
+    assert C == math.ceil(10 * 1 / 4) == 3
+    for e in range(spec.E):
+        for g in range(2):
+            assert o["sel"][e, g].tolist() == list(range(g * group, g * group + C))
+    dense = bf.dense_ffn(spec, inp, 0)
+    first = np.array([t % group < C for t in range(spec.T)])
+    np.testing.assert_allclose(o["out"][first], dense[first], rtol=RT, atol=1e-11)
+    assert np.all(o["out"][~first] == 0.0)
+
+
+def test_expert_choice_full_capacity_is_soft_mixture(oracle_mod):
+    """C = group: every expert takes every token, so the layer is the soft
+    mixture sum_e p_e FFN_e(x), with no renormalisation."""
+    spec = tiny(T=18, E=3, k=1, cf=3.0)
+    o = oracle_mod.ec_forward(spec, W.generate(spec, workers=1), 6)
+    assert o["C"] == 6
+    inp = W.generate(spec, workers=1)
+    mix = sum(o["probs"][:, e:e + 1] * bf.dense_ffn(spec, inp, e) for e in range(3))
+    np.testing.assert_allclose(o["out"], mix, rtol=RT, atol=1e-11)
+
+
+@pytest.mark.parametrize("group,k,E,cf,C", [(2048, 2, 8, 0.0, 512), (2048, 2, 8, 1.25, 640),
+                                            (16384, 1, 128, 1.0, 128), (7, 1, 8, 0.0, 1),
+                                            (10, 8, 8, 2.0, 10), (100, 3, 7, 1.0, 43)])
+def test_expert_choice_capacity_values(oracle_mod, group, k, E, cf, C):
+    spec = tiny(T=group, E=E, k=k, cf=cf)
+    assert oracle_mod.ec_capacity(spec, group) == C

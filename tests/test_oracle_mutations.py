@@ -34,6 +34,18 @@ MUTANTS = {
     "aux_counts_after_capacity": (
         "acc += ((double)c / (double)(T * k))",
         "acc += ((double)(c < orc_capacity(p) ? c : orc_capacity(p)) / (double)(T * k))"),
+    "ec_ties_to_higher_token": (
+        "if (best < 0 || logits[(g * G + i) * E + e] > logits[(g * G + best) * E + e])",
+        "if (best < 0 || logits[(g * G + i) * E + e] >= logits[(g * G + best) * E + e])"),
+    "ec_ranked_by_probs": (
+        "if (best < 0 || logits[(g * G + i) * E + e] > logits[(g * G + best) * E + e])",
+        "if (best < 0 || probs[(g * G + i) * E + e] > probs[(g * G + best) * E + e])"),
+    "ec_capacity_floor": ("double c = ceil(cf * (double)group * (double)p->k / (double)p->E);",
+                          "double c = floor(cf * (double)group * (double)p->k / (double)p->E);"),
+    "ec_weights_unnormalised": ("probs[t * E + e] = exp(l[e] - m) / Z;",
+                                "probs[t * E + e] = exp(l[e] - m);"),
+    "ec_rows_group_major": ("const int64_t row = (e * ng + g) * C + j;",
+                            "const int64_t row = (g * E + e) * C + j;"),
     "slot_weights_swapped": ("const double w = topk_w[t * k + s];",
                              "const double w = topk_w[t * k + (k - 1 - s)];"),
 }
