@@ -145,14 +145,23 @@ def cpu_baseline(spec, inp, target_s: float):
     import oracle as om
     t0 = time.perf_counter()
     lg = om.logits(spec, inp["x"], inp["Wg"], inp["bg"])
-    r = om.route(spec, lg)
-    dsp = om.dispatch(spec, r["topk_idx"])
+    if spec.ec_group:
+        r = om.expert_choice(spec, lg, spec.ec_group)
+        kept_mask = r["rowof"] >= 0
+    else:
+        r = om.route(spec, lg)
+        dsp = om.dispatch(spec, r["topk_idx"])
+        kept_mask = dsp["pos"] >= 0
     t_route = time.perf_counter() - t0
 
     def ffn(n):
         t1 = time.perf_counter()
-        om.forward_tokens(spec, inp["x"], r["topk_idx"], r["topk_w"], dsp["pos"], inp["W1"],
-                          inp.get("b1"), inp["W2"], inp.get("b2"), np.arange(n))
+        if spec.ec_group:
+            om.ec_forward_tokens(spec, inp["x"], r["rowof"], r["probs"], inp["W1"],
+                                 inp.get("b1"), inp["W2"], inp.get("b2"), np.arange(n))
+        else:
+            om.forward_tokens(spec, inp["x"], r["topk_idx"], r["topk_w"], dsp["pos"], inp["W1"],
+                              inp.get("b1"), inp["W2"], inp.get("b2"), np.arange(n))
         return time.perf_counter() - t1
 
     threads = om.num_threads()
@@ -162,7 +171,7 @@ def cpu_baseline(spec, inp, target_s: float):
     t_ffn = ffn(n) if n > n0 else t_probe
     per_tok = t_ffn / n
     total = t_route + per_tok * spec.T
-    kept = int((dsp["pos"][:n] >= 0).sum())                 # kept pairs of the sample
+    kept = int(kept_mask[:n].sum())                          # kept pairs of the sample
     flops = 2.0 * spec.T * spec.H * spec.E + 4.0 * spec.H * spec.F * kept
     cpu = "unknown"
     try:
@@ -175,10 +184,25 @@ def cpu_baseline(spec, inp, target_s: float):
         pass
     return {"value": spec.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu": cpu, "gflops": flops / (t_route + t_ffn) / 1e9,
-            "sample": (f"fp64 C oracle, {threads} OpenMP threads: gate/softmax/top-k/losses/"
-                       f"dispatch over all {spec.T} tokens ({t_route:.2f} s) + expert FFN and "
+            "sample": (f"fp64 C oracle, {threads} OpenMP threads: "
+                       f"{'gate/softmax/expert choice' if spec.ec_group else 'gate/softmax/top-k/losses/dispatch'}"
+                       f" over all {spec.T} tokens ({t_route:.2f} s) + expert FFN and "
                        f"combine on tokens 0..{n - 1} ({t_ffn:.2f} s), FFN time scaled "
                        f"linearly to {spec.T} tokens")}
+
+
+def _token_choice_calls(moe, prob, d, ws, out, losses, idx, tw, counts, offsets, pos, row_token,
+                        xp, h, y):
+    return {
+        "forward": lambda: moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"],
+                                           d["W2"], d["b2"], out, losses, ws),
+        "route": lambda: moe.moe_route(prob, d["x"], d["Wg"], d["bg"], None, idx, tw, counts,
+                                       losses, ws),
+        "permute": lambda: moe.moe_permute(prob, d["x"], idx, offsets, pos, row_token, xp, ws),
+        "expert_ffn": lambda: moe.moe_expert_ffn(prob, xp, offsets, d["W1"], d["b1"], d["W2"],
+                                                 d["b2"], h, y, ws),
+        "combine": lambda: moe.moe_combine(prob, y, pos, tw, out),
+    }
 
 
 def stage_timing(moe, torch, spec, prob, d, log_fn, min_iters=50, min_seconds=0.5):
@@ -203,20 +227,28 @@ def stage_timing(moe, torch, spec, prob, d, log_fn, min_iters=50, min_seconds=0.
     xp = torch.empty(T * k, H, dtype=sd, device=cu)
     h = torch.empty(T * k, F, dtype=sd, device=cu)
     y = torch.empty(T * k, H, dtype=sd, device=cu)
-    calls = {
-        "forward": lambda: moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"],
-                                           d["W2"], d["b2"], out, losses, ws),
-        "route": lambda: moe.moe_route(prob, d["x"], d["Wg"], d["bg"], None, idx, tw, counts,
-                                       losses, ws),
-        "permute": lambda: moe.moe_permute(prob, d["x"], idx, offsets, pos, row_token, xp, ws),
-        "expert_ffn": lambda: moe.moe_expert_ffn(prob, xp, offsets, d["W1"], d["b1"], d["W2"],
-                                                 d["b2"], h, y, ws),
-        "combine": lambda: moe.moe_combine(prob, y, pos, tw, out),
-    }
-    for name in ("route", "permute", "expert_ffn", "combine"):   # inputs of the later stages
-        calls[name]()
-    torch.cuda.synchronize()
-    A = int(offsets[-1].item())
+    if spec.ec_group:
+        # expert choice: the whole layer and its routing call
+        g = spec.ec_group
+        C = moe.moe_ec_capacity(prob, g)
+        ws = torch.empty(moe.moe_ec_workspace_bytes(prob, g), dtype=torch.uint8, device=cu)
+        probs = torch.empty(T, E, dtype=torch.float32, device=cu)
+        rowof = torch.empty(T, E, dtype=torch.int32, device=cu)
+        sel = torch.empty(E * (T // g) * C, dtype=torch.int32, device=cu)
+        calls = {
+            "forward": lambda: moe.moe_forward_expert_choice(
+                prob, g, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], out, ws),
+            "route": lambda: moe.moe_route_expert_choice(prob, g, d["x"], d["Wg"], d["bg"], None,
+                                                         probs, sel, rowof, offsets, ws),
+        }
+        A = E * (T // g) * C
+    else:
+        calls = _token_choice_calls(moe, prob, d, ws, out, losses, idx, tw, counts, offsets, pos,
+                                    row_token, xp, h, y)
+        for name in ("route", "permute", "expert_ffn", "combine"):   # inputs of later stages
+            calls[name]()
+        torch.cuda.synchronize()
+        A = int(offsets[-1].item())
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=cu)
     res = {}
     for name, fn in calls.items():
@@ -295,15 +327,21 @@ def main():
 
     d = {kk: dev(v) for kk, v in inp.items()}
     prob = moe.Problem.from_spec(spec)
-    ws = torch.empty(moe.moe_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    g = spec.ec_group
+    ws_bytes = moe.moe_ec_workspace_bytes(prob, g) if g else moe.moe_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=sd, device="cuda")
     losses = torch.empty(2, dtype=torch.float32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     evs = [moe.StageEvents() for _ in range(args.steps)]
 
     def step(ev=None):
-        moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"], out,
-                        losses, ws, offsets=offsets, events=ev)
+        if g:       # expert choice: every expert takes C tokens of each group
+            moe.moe_forward_expert_choice(prob, g, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"],
+                                          d["W2"], d["b2"], out, ws, events=ev)
+        else:
+            moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"],
+                            out, losses, ws, offsets=offsets, events=ev)
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -331,7 +369,10 @@ def main():
         abi, A_abi = stage_timing(moe, torch, spec, prob, d, log)
     stage = np.array([ev.stage_ms() for ev in evs])          # [steps][stages]
     stage_mean = stage.mean(axis=0)
-    A = int(offsets[-1].item())
+    if g:
+        A = E * (T // g) * moe.moe_ec_capacity(prob, g)
+    else:
+        A = int(offsets[-1].item())
     names = moe.STAGE_NAMES
     sm = {n: float(v) for n, v in zip(names, stage_mean)}
     gemm_flops = 2.0 * A * H * F                              # per GEMM launch
@@ -342,7 +383,7 @@ def main():
     # Each GEMM launch reads the weights of the experts that got rows and the
     # A rows of its input, and writes A rows: with few rows per expert that
     # stream, not the MFMAs, bounds it.
-    active = int(np.sum(np.diff(offsets.cpu().numpy()) > 0))
+    active = E if g else int(np.sum(np.diff(offsets.cpu().numpy()) > 0))
     gemm_bytes = active * H * F * s + A * (H + F) * s
     bound = "mfma" if gemm_flops / (PEAK_BF16_TFLOPS * 1e12) >= gemm_bytes / (PEAK_HBM_GBS * 1e9) \
         else "hbm"
@@ -351,15 +392,25 @@ def main():
     else:
         achieved, peak, unit = gemm_bytes / (sm[dom] * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     nblk = (T + 15) // 16                                     # router blocks = dispatch chunks
-    alg_bytes = {
-        # x and the gate in; top-k ids and weights, per-block partials out
-        "route": T * H * s + H * E * s + T * k * 8 + nblk * (2 * E + 1) * 4,
-        # block histograms in, chunk bases out and back in, ids in, pos and
-        # row_token out (the row gather is fused into ffn_up in moe_forward)
-        "permute": 3 * nblk * E * 4 + T * k * 8 + A * 4,
-        # kept expert rows in, slot rows and weights in, token rows out
-        "combine": A * H * s + T * k * 8 + T * H * s,
-    }
+    if g:
+        alg_bytes = {
+            # x and the gate in; fp32 logits, top-k scratch and partials out
+            "route": T * H * s + H * E * s + T * E * 4 + T * k * 8 + nblk * (2 * E + 1) * 4,
+            # logits in; probs, rowof and the selected tokens out
+            "permute": 3 * T * E * 4 + A * 4,
+            # selected rows in, rowof and probs in, token rows out
+            "combine": A * H * s + T * E * 8 + T * H * s,
+        }
+    else:
+        alg_bytes = {
+            # x and the gate in; top-k ids and weights, per-block partials out
+            "route": T * H * s + H * E * s + T * k * 8 + nblk * (2 * E + 1) * 4,
+            # block histograms in, chunk bases out and back in, ids in, pos and
+            # row_token out (the row gather is fused into ffn_up in moe_forward)
+            "permute": 3 * nblk * E * 4 + T * k * 8 + A * 4,
+            # kept expert rows in, slot rows and weights in, token rows out
+            "combine": A * H * s + T * k * 8 + T * H * s,
+        }
     hbm = {n: {"ms": sm[n], "GB/s": alg_bytes[n] / (sm[n] * 1e-3) / 1e9,
                "frac": alg_bytes[n] / (sm[n] * 1e-3) / 1e9 / PEAK_HBM_GBS} for n in alg_bytes}
     kern = "ffn_gemm_bf16_up" if dom == "ffn_up" else "ffn_gemm_bf16_down"
@@ -377,7 +428,8 @@ def main():
         "dtype": spec.dtype,
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": spec.name, "T": T, "H": H, "E": E, "k": k, "F": F,
-                   "capacity_factor": spec.cf, "activation": spec.act, "kept_rows": A},
+                   "capacity_factor": spec.cf, "activation": spec.act, "kept_rows": A,
+                   "routing": f"expert choice, groups of {g}" if g else f"top-{k}"},
         "roofline": {"bound": bound, "kernel": kern, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak,
                      "traffic": traffic_for(kern, spec.name)},
@@ -386,10 +438,10 @@ def main():
         "stage_ms": sm,
         "hbm_stages": hbm,
         "abi_ms": abi,
-        "abi_ffn_tflops": None if abi is None else {
+        "abi_ffn_tflops": None if abi is None or g else {
             m: 4.0 * H * F * A_abi / (abi["expert_ffn"][m]["median"] * 1e-3) / 1e12
             for m in ("warm", "cold")},
-        "abi_hbm_frac_cold": None if abi is None else {
+        "abi_hbm_frac_cold": None if abi is None or g else {
             "route": (T * H * s + H * E * s + T * k * 8) / (abi["route"]["cold"]["median"] * 1e-3)
                      / 1e9 / PEAK_HBM_GBS,
             "permute": (T * k * 4 + T * H * s + A_abi * H * s + 2 * A_abi * 4)
@@ -397,7 +449,7 @@ def main():
             "combine": (A_abi * H * s + T * k * 8 + T * H * s)
                        / (abi["combine"]["cold"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
-        "losses": [float(v) for v in losses.cpu().numpy()],
+        "losses": None if g else [float(v) for v in losses.cpu().numpy()],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

@@ -179,6 +179,58 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg,
                          int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
                          hipStream_t stream, hipEvent_t* stage_events);
 
+/* ------------------------------------------------------------ expert choice
+ * Expert-choice routing (Core Concepts, 2. Routing Mechanisms: the experts
+ * choose their top tokens instead of each token choosing its top experts,
+ * which balances the load exactly).  The T tokens form T / group groups of
+ * `group` consecutive tokens (a sequence each; group = T for one group).  In
+ * every group each expert takes the C tokens with the largest gate logits
+ * l[t][e] (the page ranks the raw router output over the sequence axis);
+ * equal logits go to the lower token.  Expert e's selected rows are
+ *   r = (e * (T / group) + g) * C + j,  j = 0 .. C-1,
+ * token-ascending within each (expert, group), so offsets[e] = e * (T/group) * C
+ * and every expert holds the same number of rows.  A token's output is the
+ * sum, over the experts that took it in expert order, of its softmax gate
+ * probability times that expert's output (no renormalisation; a token no
+ * expert took gets a zero row).
+ *   C = ceil(capacity_factor * group * k / E) in double, capacity_factor <= 0
+ *       read as 1 (each expert takes its balanced share), clamped to [1, group];
+ *       here k is the average number of experts per token.
+ * Extra errors: group < 1 or T % group != 0 -> MOE_ERR_INVALID_ARG;
+ * group > 32768, T * E >= 2^31 or more than 2^31 - 1 selected rows ->
+ * MOE_ERR_UNSUPPORTED. */
+
+/* C for this problem and group (host, synchronous). */
+moe_status_t moe_ec_capacity(const moe_problem_t* p, int64_t group, int64_t* C /* host */);
+
+/* Workspace bytes (host, synchronous) for both expert-choice calls below. */
+moe_status_t moe_ec_workspace_bytes(const moe_problem_t* p, int64_t group,
+                                    size_t* bytes /* host */);
+
+/* Gate logits (as moe_route; fp32 [T][E], optional output, or the input when
+ * flags has MOE_ROUTE_LOGITS_IN), then expert choice: probs[T][E] fp32 (each
+ * token's softmax over the experts), sel[E][T/group][C] int32 (the taken
+ * tokens), rowof[T][E] int32 (the row of each taken (token, expert), -1 where
+ * not taken) and offsets[E+1] int32.  Selection decides on the fp32 logits. */
+moe_status_t moe_route_expert_choice(const moe_problem_t* p, int64_t group, const void* x,
+                                     const void* Wg, const void* bg, float* logits,
+                                     uint32_t flags, float* probs, int32_t* sel,
+                                     int32_t* rowof, int32_t* offsets, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* The expert-choice layer: moe_route_expert_choice, the grouped expert FFN
+ * (Linear -> activation -> Linear) over the E * (T/group) * C selected rows,
+ * gathering x by token inside the first GEMM, and the weighted combine into
+ * out[T][H].  logits, probs, sel and rowof are optional outputs (NULL keeps
+ * them in the workspace).  stage_events as for moe_forward, with the
+ * MOE_EV_PERMUTE stage holding the expert-choice selection. */
+moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, const void* x,
+                                       const void* Wg, const void* bg, const void* W1,
+                                       const void* b1, const void* W2, const void* b2,
+                                       void* out, float* logits, float* probs, int32_t* sel,
+                                       int32_t* rowof, void* ws, size_t ws_bytes,
+                                       hipStream_t stream, hipEvent_t* stage_events);
+
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
 

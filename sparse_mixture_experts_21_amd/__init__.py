@@ -30,7 +30,9 @@ STAGE_NAMES = ("route", "permute", "ffn_up", "ffn_up_fixup", "ffn_down", "ffn_do
                "combine")
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
+           "moe_ec_capacity", "moe_ec_workspace_bytes", "moe_route_expert_choice",
+           "moe_forward_expert_choice")
 
 
 class MoeError(RuntimeError):
@@ -92,8 +94,16 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp, vp]
+        i64 = ctypes.c_int64
+        L.moe_ec_capacity.argtypes = [P, i64, ctypes.POINTER(i64)]
+        L.moe_ec_workspace_bytes.argtypes = [P, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_route_expert_choice.argtypes = [P, i64, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,
+                                              vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_forward_expert_choice.argtypes = [P, i64] + [vp] * 13 + [ctypes.c_size_t, vp, vp]
         for f in ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
-                  "moe_expert_ffn", "moe_combine", "moe_forward"):
+                  "moe_expert_ffn", "moe_combine", "moe_forward", "moe_ec_capacity",
+                  "moe_ec_workspace_bytes", "moe_route_expert_choice",
+                  "moe_forward_expert_choice"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes = [st]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -188,6 +198,40 @@ def moe_forward(p: Problem, x, Wg, bg, W1, b1, W2, b2, out, losses, ws, logits=N
                              _ptr(pos), _ptr(ws), _nbytes(ws), _stream(stream, out),
                              ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None),
            "moe_forward")
+
+
+def moe_ec_capacity(p: Problem, group: int) -> int:
+    c = ctypes.c_int64()
+    _check(lib().moe_ec_capacity(ctypes.byref(p), int(group), ctypes.byref(c)),
+           "moe_ec_capacity")
+    return c.value
+
+
+def moe_ec_workspace_bytes(p: Problem, group: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_ec_workspace_bytes(ctypes.byref(p), int(group), ctypes.byref(n)),
+           "moe_ec_workspace_bytes")
+    return n.value
+
+
+def moe_route_expert_choice(p: Problem, group: int, x, Wg, bg, logits, probs, sel, rowof,
+                            offsets, ws, flags: int = 0, stream=None) -> None:
+    _check(lib().moe_route_expert_choice(ctypes.byref(p), int(group), _ptr(x), _ptr(Wg),
+                                         _ptr(bg), _ptr(logits), flags, _ptr(probs), _ptr(sel),
+                                         _ptr(rowof), _ptr(offsets), _ptr(ws), _nbytes(ws),
+                                         _stream(stream, probs)), "moe_route_expert_choice")
+
+
+def moe_forward_expert_choice(p: Problem, group: int, x, Wg, bg, W1, b1, W2, b2, out, ws,
+                              logits=None, probs=None, sel=None, rowof=None, stream=None,
+                              events: Optional["StageEvents"] = None) -> None:
+    ev = events.array() if events is not None else None
+    _check(lib().moe_forward_expert_choice(
+        ctypes.byref(p), int(group), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1), _ptr(W2),
+        _ptr(b2), _ptr(out), _ptr(logits), _ptr(probs), _ptr(sel), _ptr(rowof), _ptr(ws),
+        _nbytes(ws), _stream(stream, out),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None),
+        "moe_forward_expert_choice")
 
 
 # ---------------------------------------------------------------- stage events

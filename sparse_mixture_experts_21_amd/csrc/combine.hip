@@ -25,9 +25,11 @@ __device__ __forceinline__ void st_stream(V* p, V v) {
 }
 
 // One workgroup = one token row; a thread owns kCombVec 16-byte vectors
-// (8 bf16 or 4 fp32 each) per pass.  The token's k (row, weight) pairs are
-// workgroup-uniform; every kept slot's vectors are loaded before the sum,
-// which runs in fp32 in slot order and is rounded once.
+// (8 bf16 or 4 fp32 each) per pass.  The token's (row, weight) pairs are
+// workgroup-uniform and taken kMaxK slots at a time (one chunk for top-k
+// routing; expert choice passes one slot per expert); every kept slot's
+// vectors of a chunk are loaded before they are added, in fp32 and in slot
+// order, and the sum is rounded once.
 constexpr int kCombThreads = 256;
 constexpr int kCombVec = 2;
 
@@ -38,51 +40,60 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __re
                                                              int k, int64_t vec,
                                                              u32x4_t* __restrict__ out) {
     const int64_t t = blockIdx.x;
-    int32_t row[kMaxK];
-    float w[kMaxK];
-#pragma unroll
-    for (int s = 0; s < kMaxK; ++s) {
-        row[s] = s < k ? pos[t * k + s] : -1;
-        w[s] = s < k ? topk_w[t * k + s] : 0.f;
-    }
     for (int64_t v0 = threadIdx.x; v0 < vec; v0 += kCombThreads * kCombVec) {
-        u32x4_t d[kMaxK][kCombVec];
+        float acc[kCombVec][8];
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
-            if (row[s] < 0) continue;                  // uniform: no divergence
+        for (int u = 0; u < kCombVec; ++u)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
+        for (int s0 = 0; s0 < k; s0 += kMaxK) {
+            int32_t row[kMaxK];
+            float w[kMaxK];
+#pragma unroll
+            for (int s = 0; s < kMaxK; ++s) {
+                row[s] = s0 + s < k ? pos[t * k + s0 + s] : -1;
+                w[s] = s0 + s < k ? topk_w[t * k + s0 + s] : 0.f;
+            }
+            u32x4_t d[kMaxK][kCombVec];
+#pragma unroll
+            for (int s = 0; s < kMaxK; ++s) {
+                if (row[s] < 0) continue;              // uniform: no divergence
+#pragma unroll
+                for (int u = 0; u < kCombVec; ++u) {
+                    const int64_t v = v0 + (int64_t)u * kCombThreads;
+                    if (v < vec) d[s][u] = ld_stream(&y[(int64_t)row[s] * vec + v]);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < kCombVec; ++u) {
-                const int64_t v = v0 + (int64_t)u * kCombThreads;
-                if (v < vec) d[s][u] = ld_stream(&y[(int64_t)row[s] * vec + v]);
+#pragma unroll
+                for (int s = 0; s < kMaxK; ++s) {
+                    if (row[s] < 0) continue;
+                    if (BF16) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[u][2 * q] = fmaf(w[s], bf16_lo(d[s][u][q]), acc[u][2 * q]);
+                            acc[u][2 * q + 1] = fmaf(w[s], bf16_hi(d[s][u][q]), acc[u][2 * q + 1]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[u][q] = fmaf(w[s], __uint_as_float(d[s][u][q]), acc[u][q]);
+                    }
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < kCombVec; ++u) {
             const int64_t v = v0 + (int64_t)u * kCombThreads;
             if (v >= vec) continue;
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < kMaxK; ++s) {
-                if (row[s] < 0) continue;
-                if (BF16) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[2 * q] = fmaf(w[s], bf16_lo(d[s][u][q]), acc[2 * q]);
-                        acc[2 * q + 1] = fmaf(w[s], bf16_hi(d[s][u][q]), acc[2 * q + 1]);
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[q] = fmaf(w[s], __uint_as_float(d[s][u][q]), acc[q]);
-                }
-            }
             u32x4_t o;
             if (BF16) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+                for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[u][q]);
             }
             st_stream(&out[t * vec + v], o);
         }

@@ -88,6 +88,75 @@ moe_status_t check_problem(const moe_problem_t* p) {
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- expert choice
+constexpr int64_t kEcMaxGroup = 32768;    // keys of one (expert, group) held in LDS
+
+int64_t ec_capacity_of(const moe_problem_t& p, int64_t group) {
+    const double cf = p.capacity_factor > 0.0 ? p.capacity_factor : 1.0;
+    double c = std::ceil(cf * (double)group * (double)p.k / (double)p.E);
+    if (c < 1.0) c = 1.0;
+    if (c > (double)group) c = (double)group;
+    return (int64_t)c;
+}
+
+// Workspace of the expert-choice calls: the router's regions of ws_layout
+// first, then logits, probs, rowof, sel, offsets, the router's top-k scratch,
+// the GEMM partials and the h / y rows.  `pg` is the problem the grouped GEMMs
+// see: k rounded up so that T * k covers the A selected rows, no capacity.
+struct EcLayout {
+    size_t logits, probs, rowof, sel, offsets, topk_idx, topk_w, part, h, y;
+    size_t route_total, total;
+    int64_t C, A;
+    moe_problem_t pg;
+    WsLayout L;
+};
+
+EcLayout ec_layout(const moe_problem_t& p, int64_t group) {
+    EcLayout X;
+    X.L = ws_layout(p);
+    const size_t T = (size_t)p.T, E = (size_t)p.E, k = (size_t)p.k, H = (size_t)p.H,
+                 F = (size_t)p.F;
+    const size_t s = p.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    X.C = ec_capacity_of(p, group);
+    X.A = (int64_t)E * (p.T / group) * X.C;
+    X.pg = p;
+    X.pg.k = (int32_t)((X.A + p.T - 1) / p.T);
+    X.pg.capacity_factor = 0.0;
+    size_t off = X.L.route_bytes;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t A = (size_t)X.A;
+    X.logits = take(T * E * 4);
+    X.probs = take(T * E * 4);
+    X.rowof = take(T * E * 4);
+    X.sel = take(A * 4);
+    X.offsets = take((E + 1) * 4);
+    X.topk_idx = take(T * k * 4);
+    X.topk_w = take(T * k * 4);
+    X.route_total = off;
+    X.part = take(gemm_partial_bytes(X.pg));
+    X.h = take(A * F * s);
+    X.y = take(A * H * s);
+    X.total = off;
+    return X;
+}
+
+moe_status_t check_group(const moe_problem_t* p, int64_t group) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (group < 1 || p->T % group != 0) return MOE_ERR_INVALID_ARG;
+    if (group > kEcMaxGroup) return MOE_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 31;
+    if (p->T * (int64_t)p->E >= lim) return MOE_ERR_UNSUPPORTED;
+    const int64_t A = (int64_t)p->E * (p->T / group) * ec_capacity_of(*p, group);
+    const int64_t tiles = (A / 64 + p->E + 1) * (((int64_t)std::max(p->H, p->F) + 255) / 256);
+    if (A >= lim || tiles + 256 >= lim) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 int64_t capacity_of(const moe_problem_t& p) {
     if (!(p.capacity_factor > 0.0)) return p.T;
     const double c = std::ceil(p.capacity_factor * (double)(p.T * (int64_t)p.k) / (double)p.E);
@@ -242,6 +311,103 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
     if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
     if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_END);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_ec_capacity(const moe_problem_t* p, int64_t group, int64_t* C) {
+    moe_status_t st = check_group(p, group);
+    if (st != MOE_OK) return st;
+    if (!C) return MOE_ERR_INVALID_ARG;
+    *C = ec_capacity_of(*p, group);
+    return MOE_OK;
+}
+
+moe_status_t moe_ec_workspace_bytes(const moe_problem_t* p, int64_t group, size_t* bytes) {
+    moe_status_t st = check_group(p, group);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = ec_layout(*p, group).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_route_expert_choice(const moe_problem_t* p, int64_t group, const void* x,
+                                     const void* Wg, const void* bg, float* logits,
+                                     uint32_t flags, float* probs, int32_t* sel, int32_t* rowof,
+                                     int32_t* offsets, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    moe_status_t st = check_group(p, group);
+    if (st != MOE_OK) return st;
+    if (flags & ~MOE_ROUTE_LOGITS_IN) return MOE_ERR_INVALID_ARG;
+    const bool logits_in = (flags & MOE_ROUTE_LOGITS_IN) != 0;
+    if (!probs || !sel || !rowof || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+    if (logits_in ? !logits : (!x || !Wg)) return MOE_ERR_INVALID_ARG;
+    if (!opt_ok(x) || !opt_ok(Wg) || !opt_ok(bg) || !opt_ok(logits) || !aligned16(probs) ||
+        !aligned16(sel) || !aligned16(rowof) || !aligned16(offsets) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const EcLayout X = ec_layout(*p, group);
+    if (ws_bytes < X.route_total) return MOE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    float* lg = logits ? logits : reinterpret_cast<float*>(w + X.logits);
+    hipError_t e = hipSuccess;
+    if (!logits_in)
+        e = launch_route(*p, X.L, w, x, Wg, bg, lg, false,
+                         reinterpret_cast<int32_t*>(w + X.topk_idx),
+                         reinterpret_cast<float*>(w + X.topk_w), nullptr, nullptr, false, stream);
+    if (e == hipSuccess)
+        e = launch_expert_choice(*p, group, X.C, lg, probs, sel, rowof, offsets, stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, const void* x,
+                                       const void* Wg, const void* bg, const void* W1,
+                                       const void* b1, const void* W2, const void* b2,
+                                       void* out, float* logits, float* probs, int32_t* sel,
+                                       int32_t* rowof, void* ws, size_t ws_bytes,
+                                       hipStream_t stream, hipEvent_t* stage_events) {
+    moe_status_t st = check_group(p, group);
+    if (st != MOE_OK) return st;
+    if (!x || !Wg || !W1 || !W2 || !out || !ws) return MOE_ERR_INVALID_ARG;
+    if (stage_events) {
+        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    }
+    if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
+        !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !opt_ok(logits) || !opt_ok(probs) ||
+        !opt_ok(sel) || !opt_ok(rowof) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const EcLayout X = ec_layout(*p, group);
+    if (ws_bytes < X.total) return MOE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    float* lg = logits ? logits : reinterpret_cast<float*>(w + X.logits);
+    float* pr = probs ? probs : reinterpret_cast<float*>(w + X.probs);
+    int32_t* sl = sel ? sel : reinterpret_cast<int32_t*>(w + X.sel);
+    int32_t* ro = rowof ? rowof : reinterpret_cast<int32_t*>(w + X.rowof);
+    int32_t* off = reinterpret_cast<int32_t*>(w + X.offsets);
+    float* part = reinterpret_cast<float*>(w + X.part);
+    void* h = w + X.h;
+    void* y = w + X.y;
+    moe_problem_t pc = *p;                 // combine: one slot per expert
+    pc.k = p->E;
+
+    auto ev = [&](int i) -> hipError_t {
+        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+    };
+    hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
+    hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
+    hipError_t e = ev(MOE_EV_ROUTE);
+    if (e == hipSuccess)
+        e = launch_route(*p, X.L, w, x, Wg, bg, lg, false,
+                         reinterpret_cast<int32_t*>(w + X.topk_idx),
+                         reinterpret_cast<float*>(w + X.topk_w), nullptr, nullptr, false, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
+    if (e == hipSuccess) e = launch_expert_choice(*p, group, X.C, lg, pr, sl, ro, off, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
+    if (e == hipSuccess) e = launch_ffn_up(X.pg, x, sl, off, W1, b1, h, part, up_fix, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
+    if (e == hipSuccess) e = launch_ffn_down(X.pg, h, off, W2, b2, y, part, down_fix, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
+    if (e == hipSuccess) e = launch_combine(pc, y, ro, pr, out, stream);
     if (e == hipSuccess) e = ev(MOE_EV_END);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

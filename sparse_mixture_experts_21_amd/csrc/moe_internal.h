@@ -86,7 +86,14 @@ hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t*
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
                            hipStream_t s);
 size_t gemm_partial_bytes(const moe_problem_t& p);
+// out[t] = sum over the k slots s of row t, in order, with pos[t][s] >= 0 of
+// topk_w[t][s] * y[pos[t][s]]; any k (expert choice passes k = E).
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s);
+// Expert choice on fp32 logits [T][E]: probs [T][E], sel [E][T/group][C],
+// rowof [T][E] (-1 where not taken) and offsets [E+1] (e * (T/group) * C).
+hipError_t launch_expert_choice(const moe_problem_t& p, int64_t group, int64_t C,
+                                const float* logits, float* probs, int32_t* sel,
+                                int32_t* rowof, int32_t* offsets, hipStream_t s);
 
 }  // namespace moe

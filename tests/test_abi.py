@@ -230,3 +230,87 @@ def test_binding_raises_on_error():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_workspace_bytes(P(k=0))
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- expert choice
+def ec_route(p, group, x=A, Wg=A, bg=None, logits=None, flags=0, probs=A, sel=A, rowof=A,
+             off=A, ws=A, ws_bytes=1 << 40):
+    return moe.lib().moe_route_expert_choice(ctypes.byref(p), group, x, Wg, bg, logits, flags,
+                                             probs, sel, rowof, off, ws, ws_bytes, None)
+
+
+def ec_forward(p, group, ws_bytes=1 << 40, **kw):
+    a = dict(x=A, Wg=A, bg=None, W1=A, b1=None, W2=A, b2=None, out=A, logits=None, probs=None,
+             sel=None, rowof=None, ws=A, ev=None)
+    a.update(kw)
+    return moe.lib().moe_forward_expert_choice(
+        ctypes.byref(p), group, a["x"], a["Wg"], a["bg"], a["W1"], a["b1"], a["W2"], a["b2"],
+        a["out"], a["logits"], a["probs"], a["sel"], a["rowof"], a["ws"], ws_bytes, None, a["ev"])
+
+
+EC_BAD = [
+    (dict(), 0, moe.MOE_ERR_INVALID_ARG),
+    (dict(), -64, moe.MOE_ERR_INVALID_ARG),
+    (dict(T=64), 48, moe.MOE_ERR_INVALID_ARG),             # T % group != 0
+    (dict(k=0), 64, moe.MOE_ERR_INVALID_ARG),              # the problem itself
+    (dict(T=65536), 65536, moe.MOE_ERR_UNSUPPORTED),       # group keys exceed LDS
+    (dict(H=36), 64, moe.MOE_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,group,status", EC_BAD, ids=[f"{b[0]}-{b[1]}" for b in EC_BAD])
+def test_ec_bad_group_rejected_by_every_entry_point(kw, group, status):
+    p = P(**kw)
+    c = ctypes.c_int64()
+    assert moe.lib().moe_ec_capacity(ctypes.byref(p), group, ctypes.byref(c)) == status
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_ec_workspace_bytes(ctypes.byref(p), group, ctypes.byref(n)) == status
+    assert ec_route(p, group) == status
+    assert ec_forward(p, group) == status
+
+
+@pytest.mark.parametrize("T,group,k,E,cf", [(16384, 2048, 2, 8, 0.0), (16384, 2048, 2, 8, 1.25),
+                                            (64, 64, 1, 8, 0.0), (70, 7, 1, 8, 0.0),
+                                            (40, 10, 8, 8, 2.0), (300, 100, 3, 7, 1.0)])
+def test_ec_capacity_matches_oracle(oracle_mod, T, group, k, E, cf):
+    import workloads as W
+    spec = W.Spec("ec", T=T, H=32, E=E, k=k, F=64, dtype="bf16", cf=cf, seed=1)
+    assert moe.moe_ec_capacity(P(T=T, k=k, E=E, capacity_factor=cf), group) == \
+        oracle_mod.ec_capacity(spec, group)
+
+
+@pytest.mark.parametrize("arg", ["probs", "sel", "rowof", "off", "ws"])
+def test_ec_route_null_required(arg):
+    assert ec_route(P(), 64, **{arg: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_ec_route_flags_and_logits_in():
+    assert ec_route(P(), 64, flags=2) == moe.MOE_ERR_INVALID_ARG
+    assert ec_route(P(), 64, flags=moe.MOE_ROUTE_LOGITS_IN, logits=None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert ec_route(P(), 64, x=None) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["probs", "sel", "rowof", "off", "ws", "x"])
+def test_ec_route_misaligned(arg):
+    assert ec_route(P(), 64, **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("arg", ["x", "Wg", "W1", "W2", "out", "ws"])
+def test_ec_forward_null_required(arg):
+    assert ec_forward(P(), 64, **{arg: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["x", "out", "logits", "probs", "sel", "rowof", "b1"])
+def test_ec_forward_misaligned(arg):
+    assert ec_forward(P(), 64, **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_ec_workspace_exact_size_and_null_event():
+    p = P()
+    need = moe.moe_ec_workspace_bytes(p, 64)
+    assert need % 256 == 0 and need > 0
+    assert ec_forward(p, 64, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert ec_route(p, 64, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+    arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
+    assert ec_forward(p, 64, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG

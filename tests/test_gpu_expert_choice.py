@@ -1,0 +1,171 @@
+"""GPU parity of expert-choice routing (moe_route_expert_choice and
+moe_forward_expert_choice through the C ABI) against the CPU oracle.
+
+The selection is decided on the GPU's fp32 logits, so the exact check applies
+the oracle's expert choice to those same logits: sel, rowof and offsets must
+match bit for bit, probs within 1e-5.  The logits themselves are compared with
+the oracle's fp64 logits, and the layer output with the oracle's expert-choice
+layer (on the same selection) within the storage-type tolerance.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as om
+import sparse_mixture_experts_21_amd as moe
+import workloads as W
+from gpu_util import DEV, as_f64, assert_close_storage, logits_tol, say, storage_dtype, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+    om.lib()
+
+
+def S(name, T, H, E, k, F, group, dtype="bf16", cf=0.0, seed=21, **kw):
+    s = W.Spec(name, T=T, H=H, E=E, k=k, F=F, dtype=dtype, cf=cf, seed=seed, ec_group=group)
+    if dtype == "f32":
+        s = s.replace(wg=W.Dist("uniform", 1 / np.sqrt(H)), w1=W.Dist("uniform", 1 / np.sqrt(H)),
+                      w2=W.Dist("uniform", 1 / np.sqrt(F)))
+    return s.replace(**kw) if kw else s
+
+
+SMALL = [
+    S("ec_bf16_T2048_H512_E8_k2_F2048_seq512", 2048, 512, 8, 2, 2048, 512),
+    S("ec_bf16_T1000_H264_E6_k1_F776_seq1000_cf1.5", 1000, 264, 6, 1, 776, 1000, cf=1.5,
+      bg=W.Dist("uniform", 0.05), b1=W.Dist("uniform", 0.05), b2=W.Dist("uniform", 0.05)),
+    S("ec_bf16_T512_H128_E16_k4_F256_seq64", 512, 128, 16, 4, 256, 64),
+    S("ec_bf16_T256_H64_E32_k1_F128_seq256", 256, 64, 32, 1, 128, 256, wg=W.Dist("normal", 0.1)),
+    S("ec_silu_T1024_H256_E8_k2_F512_seq128", 1024, 256, 8, 2, 512, 128, act="silu"),
+    S("ec_f32_T96_H32_E5_k2_F64_seq24", 96, 32, 5, 2, 64, 24, dtype="f32",
+      bg=W.Dist("uniform", 0.05), b1=W.Dist("uniform", 0.05), b2=W.Dist("uniform", 0.05)),
+    # one group larger than 64 KB of keys (dynamic LDS above the default limit)
+    S("ec_bf16_T32768_H64_E4_k1_F128_seq32768", 32768, 64, 4, 1, 128, 32768),
+    # all logits tie: every expert takes the first C tokens of each group
+    W.zero_gate(S("ec_zero_gate_T600_H128_E8_k2_F256_seq200", 600, 128, 8, 2, 256, 200)),
+]
+
+
+def _alloc(spec):
+    T, E, H = spec.T, spec.E, spec.H
+    C = om.ec_capacity(spec, spec.ec_group)
+    ng = T // spec.ec_group
+    return dict(logits=torch.empty(T, E, dtype=torch.float32, device=DEV),
+                probs=torch.empty(T, E, dtype=torch.float32, device=DEV),
+                sel=torch.empty(E * ng * C, dtype=torch.int32, device=DEV),
+                rowof=torch.empty(T, E, dtype=torch.int32, device=DEV),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+                out=torch.empty(T, H, dtype=storage_dtype(spec), device=DEV))
+
+
+def _ws(prob, group):
+    return torch.empty(moe.moe_ec_workspace_bytes(prob, group), dtype=torch.uint8, device=DEV)
+
+
+def _check_selection(spec, o, what):
+    """The oracle's expert choice on the GPU's fp32 logits reproduces the GPU's
+    selection bit for bit."""
+    lg = as_f64(o["logits"])
+    r = om.expert_choice(spec, lg, spec.ec_group)
+    assert np.array_equal(o["sel"].cpu().numpy(), r["sel"].ravel()), f"{what}: sel"
+    assert np.array_equal(o["rowof"].cpu().numpy(), r["rowof"]), f"{what}: rowof"
+    np.testing.assert_allclose(o["probs"].cpu().numpy().astype(np.float64), r["probs"],
+                               rtol=0, atol=1e-5, err_msg=f"{what}: probs")
+    return r
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_ec_forward_small(spec):
+    say(f"[expert choice forward] {spec.name}")
+    g = spec.ec_group
+    inp = W.generate(spec)
+    d = upload(spec, inp)
+    prob = moe.Problem.from_spec(spec)
+    assert moe.moe_ec_capacity(prob, g) == om.ec_capacity(spec, g)
+    o = _alloc(spec)
+    ws = _ws(prob, g)
+    moe.moe_forward_expert_choice(prob, g, d["x"], d["Wg"], d.get("bg"), d["W1"], d.get("b1"),
+                                  d["W2"], d.get("b2"), o["out"], ws, logits=o["logits"],
+                                  probs=o["probs"], sel=o["sel"], rowof=o["rowof"])
+    torch.cuda.synchronize()
+    ref_lg = om.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    err = float(np.max(np.abs(as_f64(o["logits"]) - ref_lg)))
+    assert err <= logits_tol(spec), err
+    r = _check_selection(spec, o, "forward")
+    C, ng = r["C"], spec.T // g
+    # perfect balance and a bijection onto the rows
+    rows = o["rowof"].cpu().numpy()
+    assert np.array_equal(np.sort(rows[rows >= 0]), np.arange(spec.E * ng * C))
+    ref = om.ec_forward_tokens(spec, inp["x"], r["rowof"], r["probs"], inp["W1"], inp.get("b1"),
+                               inp["W2"], inp.get("b2"), np.arange(spec.T))
+    assert_close_storage(as_f64(o["out"]), ref, spec.dtype, "out")
+    if spec.wg.kind == "zero":
+        for e in range(spec.E):
+            for gi in range(ng):
+                assert r["sel"][e, gi].tolist() == list(range(gi * g, gi * g + C))
+
+
+@pytest.mark.parametrize("spec", SMALL[:4], ids=lambda s: s.name)
+def test_ec_route_equals_forward_bitwise(spec):
+    """moe_route_expert_choice alone (and fed the forward's logits back as an
+    input) gives the forward's routing outputs bit for bit; the forward is
+    deterministic."""
+    g = spec.ec_group
+    inp = W.generate(spec)
+    d = upload(spec, inp)
+    prob = moe.Problem.from_spec(spec)
+    ws = _ws(prob, g)
+    f1, f2, r1, r2 = _alloc(spec), _alloc(spec), _alloc(spec), _alloc(spec)
+    for f in (f1, f2):
+        moe.moe_forward_expert_choice(prob, g, d["x"], d["Wg"], d.get("bg"), d["W1"],
+                                      d.get("b1"), d["W2"], d.get("b2"), f["out"], ws,
+                                      logits=f["logits"], probs=f["probs"], sel=f["sel"],
+                                      rowof=f["rowof"])
+    moe.moe_route_expert_choice(prob, g, d["x"], d["Wg"], d.get("bg"), r1["logits"], r1["probs"],
+                                r1["sel"], r1["rowof"], r1["offsets"], ws)
+    r2["logits"].copy_(f1["logits"])
+    moe.moe_route_expert_choice(prob, g, None, None, None, r2["logits"], r2["probs"], r2["sel"],
+                                r2["rowof"], r2["offsets"], ws, flags=moe.MOE_ROUTE_LOGITS_IN)
+    torch.cuda.synchronize()
+    assert torch.equal(f1["out"], f2["out"])
+    for k in ("logits", "probs", "sel", "rowof"):
+        assert torch.equal(f1[k], r1[k]), k
+        assert torch.equal(f1[k], r2[k]), k
+    C = om.ec_capacity(spec, g)
+    assert r1["offsets"].cpu().tolist() == [e * (spec.T // g) * C for e in range(spec.E + 1)]
+
+
+def test_ec_full_size_sampled():
+    spec = W.CONFIGS["c5e"]
+    g = spec.ec_group
+    say(f"[expert choice full size] {spec.name}")
+    inp = W.generate(spec)
+    d = upload(spec, inp)
+    prob = moe.Problem.from_spec(spec)
+    o = _alloc(spec)
+    ws = _ws(prob, g)
+    moe.moe_forward_expert_choice(prob, g, d["x"], d["Wg"], d.get("bg"), d["W1"], d.get("b1"),
+                                  d["W2"], d.get("b2"), o["out"], ws, logits=o["logits"],
+                                  probs=o["probs"], sel=o["sel"], rowof=o["rowof"])
+    torch.cuda.synchronize()
+    ref_lg = om.logits(spec, inp["x"], inp["Wg"], inp["bg"])
+    assert float(np.max(np.abs(as_f64(o["logits"]) - ref_lg))) <= logits_tol(spec)
+    r = _check_selection(spec, o, "full size")
+    taken = (r["rowof"] >= 0).sum(axis=1)
+    say(f"    C {r['C']}, rows {spec.E * (spec.T // g) * r['C']}, tokens taken by 0 experts "
+        f"{int((taken == 0).sum())}, by >= 3 experts {int((taken >= 3).sum())}")
+    rng = np.random.default_rng(0)
+    toks = np.unique(np.concatenate([np.arange(8), np.arange(spec.T - 8, spec.T),
+                                     rng.choice(spec.T, 40, replace=False),
+                                     np.nonzero(taken == 0)[0][:4],
+                                     np.nonzero(taken == taken.max())[0][:4]]))
+    ref = om.ec_forward_tokens(spec, inp["x"], r["rowof"], r["probs"], inp["W1"], inp.get("b1"),
+                               inp["W2"], inp.get("b2"), toks)
+    got = as_f64(o["out"][torch.from_numpy(toks).to(DEV)])
+    assert_close_storage(got, ref, spec.dtype, f"out[{len(toks)} sampled tokens]")

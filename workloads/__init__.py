@@ -68,6 +68,7 @@ class Spec:
     b2: Optional[Dist] = None
     identical_experts: bool = False   # every expert gets expert 0's weights
     act: str = "gelu"                 # expert activation: "gelu" (exact erf) or "silu"
+    ec_group: int = 0                 # > 0: expert-choice routing over groups of this size
 
     def replace(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -108,6 +109,10 @@ for _t in (1, 8, 64, 256):
     CONFIGS[f"d{_t}"] = Spec(f"mixtral_decode_T{_t}_H4096_E8_k2_F14336_dropless", T=_t, H=4096,
                              E=8, k=2, F=14336, dtype="bf16", cf=0.0, seed=8)
 del _t
+# Expert-choice routing on the Mixtral-shaped layer: each expert takes its
+# C = ceil(2048 * 2 / 8) = 512 top tokens of every 2048-token sequence.
+CONFIGS["c5e"] = Spec("mixtral_expert_choice_T16384_H4096_E8_k2_F14336_seq2048", T=16384,
+                      H=4096, E=8, k=2, F=14336, dtype="bf16", cf=0.0, seed=9, ec_group=2048)
 
 
 # ----------------------------------------------------------------------------
