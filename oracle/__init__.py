@@ -54,6 +54,10 @@ def lib():
         L.orc_expert_choice.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp]
         L.orc_ec_capacity.argtypes = [P, ctypes.c_int64]
         L.orc_ec_capacity.restype = ctypes.c_int64
+        L.orc_backward.argtypes = [P] + [vp] * 8 + [vp, ctypes.c_double, ctypes.c_double] + [vp] * 7
+        L.orc_backward_tokens.argtypes = [P] + [vp] * 8 + [vp, ctypes.c_double, ctypes.c_double,
+                                                          vp, ctypes.c_int64, vp]
+        L.orc_backward_weight_entries.argtypes = [P] + [vp] * 8 + [vp, vp, ctypes.c_int64, vp]
         L.orc_num_threads.argtypes = []
         _lib = L
     return _lib
@@ -68,7 +72,8 @@ def problem(spec, **over) -> _Problem:
         raise ValueError(f"activation {act!r}")
     return _Problem(T=int(g("T")), H=int(g("H")), E=int(g("E")), k=int(g("k")),
                     F=int(g("F")), cf=float(g("cf")),
-                    dtype=1 if g("dtype") == "bf16" else 0, act=1 if act == "silu" else 0)
+                    dtype={"f32": 0, "bf16": 1, "f64": 2}[g("dtype")],
+                    act=1 if act == "silu" else 0)
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -78,7 +83,7 @@ def _ptr(a: Optional[np.ndarray]):
 def _storage(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
     if a is None:
         return None
-    want = np.uint16 if dtype == "bf16" else np.float32
+    want = {"bf16": np.uint16, "f32": np.float32, "f64": np.float64}[dtype]
     if a.dtype != want:
         raise TypeError(f"oracle expects {want} storage for {dtype}, got {a.dtype}")
     return np.ascontiguousarray(a)
@@ -243,6 +248,51 @@ def ec_forward(spec, inp: Dict[str, Optional[np.ndarray]], group: int,
     res: Dict[str, object] = dict(logits=lg, out=out, tokens=toks)
     res.update(r)
     return res
+
+
+# ---------------------------------------------------------------- backward
+def _bwd_common(spec, inp, dout, given_logits):
+    d = spec.dtype
+    lg = None if given_logits is None else np.ascontiguousarray(given_logits, np.float64)
+    return (ctypes.byref(problem(spec)), _ptr(_storage(inp["x"], d)), _ptr(_storage(inp["Wg"], d)),
+            _ptr(_storage(inp.get("bg"), d)), _ptr(_storage(inp["W1"], d)),
+            _ptr(_storage(inp.get("b1"), d)), _ptr(_storage(inp["W2"], d)),
+            _ptr(_storage(inp.get("b2"), d)), _ptr(lg), _ptr(_storage(dout, d)))
+
+
+def backward(spec, inp: Dict[str, Optional[np.ndarray]], dout: np.ndarray, g_aux: float = 0.0,
+             g_z: float = 0.0, given_logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of L = sum(dout * out) + g_aux * aux + g_z * z with respect to
+    x, the gate and the expert weights (fp64; biases only when present)."""
+    T, H, E, F = spec.T, spec.H, spec.E, spec.F
+    g = dict(dx=np.empty((T, H)), dWg=np.empty((H, E)), dbg=np.empty(E),
+             dW1=np.empty((E, H, F)), db1=np.empty((E, F)), dW2=np.empty((E, F, H)),
+             db2=np.empty((E, H)))
+    _check(lib().orc_backward(*_bwd_common(spec, inp, dout, given_logits), float(g_aux),
+                              float(g_z), *[_ptr(g[n]) for n in ("dx", "dWg", "dbg", "dW1", "db1",
+                                                                  "dW2", "db2")]), "backward")
+    return g
+
+
+def backward_tokens(spec, inp, dout, tokens: Sequence[int], g_aux: float = 0.0, g_z: float = 0.0,
+                    given_logits: Optional[np.ndarray] = None) -> np.ndarray:
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    dx = np.empty((tok.shape[0], spec.H))
+    _check(lib().orc_backward_tokens(*_bwd_common(spec, inp, dout, given_logits), float(g_aux),
+                                     float(g_z), _ptr(tok), tok.shape[0], _ptr(dx)),
+           "backward_tokens")
+    return dx
+
+
+def backward_weight_entries(spec, inp, dout, entries, given_logits=None) -> np.ndarray:
+    """entries: rows (kind, e, i, j) with kind 1 dW1[e][i][j], 2 dW2[e][i][j],
+    3 db1[e][j], 4 db2[e][j]."""
+    ent = np.ascontiguousarray(np.asarray(entries, dtype=np.int32).reshape(-1, 4))
+    out = np.empty(ent.shape[0])
+    _check(lib().orc_backward_weight_entries(*_bwd_common(spec, inp, dout, given_logits),
+                                             _ptr(ent), ent.shape[0], _ptr(out)),
+           "backward_weight_entries")
+    return out
 
 
 def topk_margin(spec, lg: np.ndarray) -> float:

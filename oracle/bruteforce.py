@@ -234,3 +234,35 @@ def torch_expert_choice_sets(lg: np.ndarray, group: int, C: int) -> np.ndarray:
     idx = torch.topk(scores, k=C, dim=-1).indices                         # (ng, E, C)
     glob = idx + (torch.arange(ng) * group)[:, None, None]
     return np.sort(glob.permute(1, 0, 2).numpy(), axis=-1)
+
+
+# ---------------------------------------------------------------- backward
+def torch_layer_grads(spec, inp: Dict[str, Optional[np.ndarray]], dout: np.ndarray,
+                      g_aux: float, g_z: float) -> Dict[str, np.ndarray]:
+    """Gradients of L = sum(dout * out) + g_aux * aux + g_z * z by torch
+    autograd in float64, for the page's layer with no capacity limit: gate
+    linear, softmax, torch.topk, renormalisation, every expert evaluated
+    densely and gathered by index, the aux loss with the routed fractions f
+    held constant, and the z-loss.  Returned in the [in][out] weight layout."""
+    import torch
+    d = spec.dtype
+    T, E, k = spec.T, spec.E, spec.k
+    t64 = lambda a: None if a is None else torch.from_numpy(_f64(a, d)).requires_grad_(True)
+    x, Wg, bg = t64(inp["x"]), t64(inp["Wg"]), t64(inp.get("bg"))
+    W1, b1, W2, b2 = t64(inp["W1"]), t64(inp.get("b1")), t64(inp["W2"]), t64(inp.get("b2"))
+    lg = x @ Wg + (bg if bg is not None else 0.0)
+    p = torch.softmax(lg, dim=1)
+    val, idx = torch.topk(p, k, dim=1)
+    w = val / val.sum(dim=1, keepdim=True)
+    act = torch.nn.functional.silu if spec.act == "silu" else torch.nn.functional.gelu
+    Y = torch.stack([act(x @ W1[e] + (b1[e] if b1 is not None else 0.0)) @ W2[e]
+                     + (b2[e] if b2 is not None else 0.0) for e in range(E)])     # [E, T, H]
+    sel = Y[idx, torch.arange(T)[:, None], :]                                      # [T, k, H]
+    out = (w[:, :, None] * sel).sum(dim=1)
+    f = torch.bincount(idx.reshape(-1), minlength=E).double() / float(T * k)
+    aux = E * (f * p.mean(dim=0)).sum()
+    z = (torch.logsumexp(lg, dim=1) ** 2).mean()
+    L = (torch.from_numpy(_f64(dout, d)) * out).sum() + g_aux * aux + g_z * z
+    L.backward()
+    g = lambda t: None if t is None else t.grad.numpy()
+    return dict(dx=g(x), dWg=g(Wg), dbg=g(bg), dW1=g(W1), db1=g(b1), dW2=g(W2), db2=g(b2))

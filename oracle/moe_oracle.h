@@ -36,7 +36,7 @@ typedef struct {
     int32_t k;      /* experts per token */
     int32_t F;      /* expert inner width (4H on the pages) */
     double  cf;     /* capacity factor; <= 0 means no capacity limit */
-    int32_t dtype;  /* 0: fp32 storage, 1: bf16 storage */
+    int32_t dtype;  /* 0: fp32 storage, 1: bf16 storage, 2: fp64 storage */
     int32_t act;    /* expert activation: 0 exact GELU, 1 SiLU */
 } orc_problem;
 
@@ -95,6 +95,34 @@ int orc_expert_choice(const orc_problem* p, int64_t group, const double* logits,
 /* Expert-choice capacity: ceil(cf * group * k / E) in double, with cf <= 0
  * read as 1 (each expert takes its balanced share), clamped to [1, group]. */
 int64_t orc_ec_capacity(const orc_problem* p, int64_t group);
+
+/* Backward of the layer ("moe-training" SKILL page: training minimises the
+ * output loss plus the weighted router losses) for the objective
+ *   L = sum_t dout[t] . out[t] + g_aux * aux + g_z * z,
+ * dout [T][H] in the storage type.  Routing is decided on logits_in [T][E]
+ * when given, else on the gate linear of x.  Outputs (double; any may be
+ * NULL): dx [T][H], dWg [H][E], dbg [E], dW1 [E][H][F], db1 [E][F],
+ * dW2 [E][F][H], db2 [E][H].  Dropped slots and the top-k selection pass no
+ * gradient; the renormalised weights, the softmax and both losses do. */
+int orc_backward(const orc_problem* p, const void* x, const void* Wg, const void* bg,
+                 const void* W1, const void* b1, const void* W2, const void* b2,
+                 const double* logits_in, const void* dout, double g_aux, double g_z,
+                 double* dx, double* dWg, double* dbg, double* dW1, double* db1, double* dW2,
+                 double* db2);
+
+/* dx rows [ntok][H] of the listed tokens only (the same definition). */
+int orc_backward_tokens(const orc_problem* p, const void* x, const void* Wg, const void* bg,
+                        const void* W1, const void* b1, const void* W2, const void* b2,
+                        const double* logits_in, const void* dout, double g_aux, double g_z,
+                        const int64_t* tokens, int64_t ntok, double* dx);
+
+/* Single entries of the expert-weight gradients: entries [n][4] = (kind, e,
+ * i, j) with kind 1: dW1[e][i][j], 2: dW2[e][i][j], 3: db1[e][j], 4: db2[e][j];
+ * each is summed over the expert's kept rows in token order. */
+int orc_backward_weight_entries(const orc_problem* p, const void* x, const void* Wg,
+                                const void* bg, const void* W1, const void* b1, const void* W2,
+                                const void* b2, const double* logits_in, const void* dout,
+                                const int32_t* entries, int64_t n, double* out);
 
 /* Number of OpenMP threads the oracle uses. */
 int orc_num_threads(void);

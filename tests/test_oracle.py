@@ -400,3 +400,107 @@ def test_expert_choice_full_capacity_is_soft_mixture(oracle_mod):
 def test_expert_choice_capacity_values(oracle_mod, group, k, E, cf, C):
     spec = tiny(T=group, E=E, k=k, cf=cf)
     assert oracle_mod.ec_capacity(spec, group) == C
+
+
+# ---------------------------------------------------------------- backward
+BWD_CASES = [
+    dict(g_aux=0.3, g_z=0.1),
+    dict(g_aux=0.0, g_z=0.0, act="silu"),
+    dict(k=1, g_aux=1.0, g_z=0.5),
+    dict(k=3, E=5, T=20, g_aux=0.01, g_z=0.001, biases=False),
+    dict(dtype="bf16", E=8, T=40, g_aux=0.2, g_z=0.2),
+    dict(E=1, k=1, T=10, g_aux=0.5, g_z=0.5),
+]
+
+
+def _bwd(case):
+    case = dict(case)
+    ga, gz = case.pop("g_aux"), case.pop("g_z")
+    spec = tiny(**case)
+    inp = W.generate(spec, workers=1)
+    dout = W.synthetic_rows(spec, spec.T, tid=91)
+    return spec, inp, dout, ga, gz
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(c) for c in BWD_CASES])
+def test_backward_matches_torch_autograd(oracle_mod, case):
+    """No capacity limit: the oracle's chain rule against torch autograd through
+    the page's layer (topk, renormalisation, dense experts, aux and z losses)."""
+    spec, inp, dout, ga, gz = _bwd(case)
+    g = oracle_mod.backward(spec, inp, dout, ga, gz)
+    t = bf.torch_layer_grads(spec, inp, dout, ga, gz)
+    for name, ref in t.items():
+        if ref is None:
+            continue
+        np.testing.assert_allclose(g[name], ref, rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def _f64_inputs(spec, inp):
+    return {k: None if v is None else W.to_f32(v, spec.dtype).astype(np.float64)
+            for k, v in inp.items()}
+
+
+def _objective(om, spec, inp, dout, ga, gz):
+    o = om.forward(spec, inp)
+    return float(np.sum(dout * o["out"])) + ga * o["aux"] + gz * o["z"]
+
+
+@pytest.mark.parametrize("cf,act", [(0.5, "gelu"), (0.75, "silu"), (0.0, "gelu")])
+def test_backward_directional_finite_differences(oracle_mod, cf, act):
+    """fp64 storage, capacity drops included: for a random direction v of each
+    input, (L(u + e v) - L(u - e v)) / 2e equals <dL/du, v> (routing and drops
+    do not change within +-e for these inputs)."""
+    spec32 = tiny(T=32, E=4, k=2, cf=cf, act=act)
+    inp = _f64_inputs(spec32, W.generate(spec32, workers=1))
+    spec = spec32.replace(dtype="f64")
+    dout = W.to_f32(W.synthetic_rows(spec32, spec32.T, tid=92), "f32").astype(np.float64)
+    ga, gz = 0.3, 0.2
+    if cf > 0:
+        o = oracle_mod.forward(spec, inp)
+        assert (o["pos"] < 0).any(), "no slot dropped: the case does not exercise drops"
+    g = oracle_mod.backward(spec, inp, dout, ga, gz)
+    rng = np.random.default_rng(5)
+    eps = 1e-6
+    for name, grad in (("x", "dx"), ("Wg", "dWg"), ("bg", "dbg"), ("W1", "dW1"), ("b1", "db1"),
+                       ("W2", "dW2"), ("b2", "db2")):
+        v = rng.standard_normal(inp[name].shape)
+        hi, lo = dict(inp), dict(inp)
+        hi[name] = inp[name] + eps * v
+        lo[name] = inp[name] - eps * v
+        fd = (_objective(oracle_mod, spec, hi, dout, ga, gz) -
+              _objective(oracle_mod, spec, lo, dout, ga, gz)) / (2 * eps)
+        an = float(np.sum(g[grad] * v))
+        assert math.isclose(fd, an, rel_tol=1e-6, abs_tol=1e-8), (name, fd, an)
+
+
+def test_backward_dropped_slots_pass_no_expert_gradient(oracle_mod):
+    """Heavy drops (cf = 0.25): an expert's weight gradients only see its kept
+    rows, so a dout that is zero on every token keeping a slot of expert e
+    leaves dW1[e], dW2[e] and the biases of e exactly zero."""
+    spec = tiny(T=40, E=4, k=2, cf=0.25)
+    inp = W.generate(spec, workers=1)
+    o = oracle_mod.forward(spec, inp)
+    e = 2
+    keep_e = np.any((o["topk_idx"] == e) & (o["pos"] >= 0), axis=1)
+    dout = W.synthetic_rows(spec, spec.T, tid=93)
+    dout[keep_e] = 0
+    g = oracle_mod.backward(spec, inp, dout, 0.0, 0.0)
+    for n in ("dW1", "db1", "dW2", "db2"):
+        assert np.all(g[n][e] == 0.0), n
+    assert np.any(g["dW1"][(e + 1) % 4] != 0.0)
+
+
+def test_backward_tokens_and_weight_entries_match_full(oracle_mod):
+    spec = tiny(T=30, E=5, k=2, cf=0.75, dtype="bf16")
+    inp = W.generate(spec, workers=1)
+    dout = W.synthetic_rows(spec, spec.T, tid=94)
+    g = oracle_mod.backward(spec, inp, dout, 0.2, 0.05)
+    toks = [0, 7, 13, 29]
+    dx = oracle_mod.backward_tokens(spec, inp, dout, toks, 0.2, 0.05)
+    np.testing.assert_allclose(dx, g["dx"][toks], rtol=1e-12, atol=1e-14)
+    ent = [(1, 0, 3, 7), (1, 4, 15, 39), (2, 2, 11, 5), (2, 3, 0, 15), (3, 1, 0, 20),
+           (4, 4, 0, 9)]
+    v = oracle_mod.backward_weight_entries(spec, inp, dout, ent)
+    ref = [g["dW1"][0, 3, 7], g["dW1"][4, 15, 39], g["dW2"][2, 11, 5], g["dW2"][3, 0, 15],
+           g["db1"][1, 20], g["db2"][4, 9]]
+    np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-14)

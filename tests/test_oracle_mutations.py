@@ -15,8 +15,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 MUTANTS = {
     "drop_expert_bias2": ("y[o] += load(b2, (int64_t)e * H + o, dt);", "y[o] += 0.0;"),
     "silu_evaluated_as_gelu": ("p->act == 1 ?", "p->act == 99 ?"),
-    "silu_wrong_sign": ("a[j] / (1.0 + exp(-a[j]))", "a[j] / (1.0 + exp(a[j]))"),
-    "gelu_wrong_sign": ("(1.0 + erf(a[j] * M_SQRT1_2))", "(1.0 - erf(a[j] * M_SQRT1_2))"),
+    "silu_wrong_sign": ("a / (1.0 + exp(-a))", "a / (1.0 + exp(a))"),
+    "gelu_wrong_sign": ("0.5 * a * (1.0 + erf(a * M_SQRT1_2))", "0.5 * a * (1.0 - erf(a * M_SQRT1_2))"),
     "aux_without_E": ("*aux = (double)E * acc;", "*aux = acc;"),
     "tie_to_higher_index": ("if (best < 0 || l[e] > l[best]) best = e;",
                             "if (best < 0 || l[e] >= l[best]) best = e;"),
@@ -46,6 +46,20 @@ MUTANTS = {
                                 "probs[t * E + e] = exp(l[e] - m);"),
     "ec_rows_group_major": ("const int64_t row = (e * ng + g) * C + j;",
                             "const int64_t row = (g * E + e) * C + j;"),
+    "bwd_gelu_grad_without_density": (
+        "+ a * exp(-0.5 * a * a) / sqrt(2.0 * M_PI);", ";"),
+    "bwd_silu_grad_is_sigmoid": ("return s * (1.0 + a * (1.0 - s));", "return s;"),
+    "bwd_renorm_without_mean": ("dp[idx[s]] += (dw[s] - sw) / S;", "dp[idx[s]] += dw[s] / S;"),
+    "bwd_aux_without_E": ("g_aux * (double)E * ((double)r->counts[e]",
+                          "g_aux * ((double)r->counts[e]"),
+    "bwd_z_without_2": ("g_z * 2.0 * r->lse[t]", "g_z * r->lse[t]"),
+    "bwd_softmax_not_centred": ("dl[e] = pt[e] * (dp[e] - pdp)", "dl[e] = pt[e] * dp[e]"),
+    "bwd_dW2_from_pre_activation": ("const double h = act_val(p, a[j]);", "const double h = a[j];"),
+    "bwd_dropped_slot_passes_gradient": (
+        "                dw[s] = 0.0;\n                if (r.pos[t * k + s] < 0) continue;\n"
+        "                const int e = r.idx[t * k + s];\n                double* a = A",
+        "                dw[s] = 0.0;\n"
+        "                const int e = r.idx[t * k + s];\n                double* a = A"),
     "slot_weights_swapped": ("const double w = topk_w[t * k + s];",
                              "const double w = topk_w[t * k + (k - 1 - s)];"),
 }
