@@ -231,6 +231,45 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, co
                                        int32_t* rowof, void* ws, size_t ws_bytes,
                                        hipStream_t stream, hipEvent_t* stage_events);
 
+/* ---------------------------------------------------------------- training
+ * The backward of the layer (the pages train it: the output's loss plus the
+ * weighted load-balancing and z losses, Core Concepts, 3. Load Balancing) for
+ *   L = sum_t dout[t] . out[t] + g_aux * aux + g_z * z.
+ * For a kept slot s of token t (expert e, weight w = p_e / S, S the sum of the
+ * k selected probabilities), with a = x W1[e] + b1[e], h = act(a) and
+ * y = h W2[e] + b2[e]:
+ *   dy = w dout[t], dw_s = dout[t] . y;  dh = dy W2[e]^T, da = dh * act'(a);
+ *   dW2[e] += h^T dy, db2[e] += dy, dW1[e] += x^T da, db1[e] += da,
+ *   dx[t] += da W1[e]^T;
+ * through the renormalisation dp_j = (dw_j - sum_s dw_s w_s) / S, the aux
+ * loss + g_aux E f_e / T (the routed fractions f held constant), the softmax
+ * dl = p (dp - p . dp) and the z-loss + g_z 2 lse p / T;
+ *   dWg += x^T dl, dbg += dl, dx[t] += dl Wg^T.
+ * Dropped slots and the top-k choice pass no gradient.
+ * bf16 storage only (fp32 problems -> MOE_ERR_UNSUPPORTED), and T * k *
+ * max(H, F) * 2 below 2^31 bytes.  dx is bf16 [T][H]; every parameter
+ * gradient is fp32 in the parameter's layout (dWg [H][E], dW1 [E][H][F],
+ * dW2 [E][F][H], biases [E], [E][F], [E][H]); the bias gradients are optional.
+ * Every gradient is written (not accumulated) and is bitwise reproducible. */
+
+/* Workspace bytes (host) for moe_forward_train and moe_backward. */
+moe_status_t moe_train_workspace_bytes(const moe_problem_t* p, size_t* bytes /* host */);
+
+/* moe_forward (out, losses) that keeps in ws what moe_backward needs: the fp32
+ * logits, routing, dispatch, the pre-activation rows a and the h and y rows. */
+moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void* Wg,
+                               const void* bg, const void* W1, const void* b1, const void* W2,
+                               const void* b2, void* out, float* losses, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Gradients of L.  ws must hold the state of a moe_forward_train on the same
+ * problem and inputs (nothing else may write it in between); biases are not
+ * needed (the saved rows already include them). */
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg, const void* W1,
+                          const void* W2, const void* dout, float g_aux, float g_z, void* dx,
+                          float* dWg, float* dbg, float* dW1, float* db1, float* dW2,
+                          float* db2, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);
 

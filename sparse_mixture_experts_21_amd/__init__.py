@@ -32,7 +32,8 @@ STAGE_NAMES = ("route", "permute", "ffn_up", "ffn_up_fixup", "ffn_down", "ffn_do
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
            "moe_ec_capacity", "moe_ec_workspace_bytes", "moe_route_expert_choice",
-           "moe_forward_expert_choice")
+           "moe_forward_expert_choice", "moe_train_workspace_bytes", "moe_forward_train",
+           "moe_backward")
 
 
 class MoeError(RuntimeError):
@@ -100,10 +101,15 @@ def lib() -> ctypes.CDLL:
         L.moe_route_expert_choice.argtypes = [P, i64, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,
                                               vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_forward_expert_choice.argtypes = [P, i64] + [vp] * 13 + [ctypes.c_size_t, vp, vp]
+        L.moe_train_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_forward_train.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
+        fl = ctypes.c_float
+        L.moe_backward.argtypes = [P] + [vp] * 5 + [fl, fl] + [vp] * 8 + [ctypes.c_size_t, vp]
         for f in ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
                   "moe_expert_ffn", "moe_combine", "moe_forward", "moe_ec_capacity",
                   "moe_ec_workspace_bytes", "moe_route_expert_choice",
-                  "moe_forward_expert_choice"):
+                  "moe_forward_expert_choice", "moe_train_workspace_bytes",
+                  "moe_forward_train", "moe_backward"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes = [st]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -232,6 +238,28 @@ def moe_forward_expert_choice(p: Problem, group: int, x, Wg, bg, W1, b1, W2, b2,
         _nbytes(ws), _stream(stream, out),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None),
         "moe_forward_expert_choice")
+
+
+def moe_train_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_train_workspace_bytes(ctypes.byref(p), ctypes.byref(n)),
+           "moe_train_workspace_bytes")
+    return n.value
+
+
+def moe_forward_train(p: Problem, x, Wg, bg, W1, b1, W2, b2, out, losses, ws, stream=None) -> None:
+    _check(lib().moe_forward_train(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1),
+                                   _ptr(b1), _ptr(W2), _ptr(b2), _ptr(out), _ptr(losses),
+                                   _ptr(ws), _nbytes(ws), _stream(stream, out)),
+           "moe_forward_train")
+
+
+def moe_backward(p: Problem, x, Wg, W1, W2, dout, g_aux, g_z, dx, dWg, dW1, dW2, ws,
+                 dbg=None, db1=None, db2=None, stream=None) -> None:
+    _check(lib().moe_backward(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(W1), _ptr(W2), _ptr(dout),
+                              float(g_aux), float(g_z), _ptr(dx), _ptr(dWg), _ptr(dbg), _ptr(dW1),
+                              _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(ws), _nbytes(ws),
+                              _stream(stream, dx)), "moe_backward")
 
 
 # ---------------------------------------------------------------- stage events

@@ -1,0 +1,335 @@
+// Grouped GEMMs of the backward ("moe-training" SKILL page: training the
+// layer; the gradients of its expert FFNs by the chain rule).  For the kept
+// rows r of expert e (offsets[e] <= r < offsets[e+1]):
+//
+//   dgrad   C[r][n] = sum_k X[r][k] B[e][n][k]      both operands K-contiguous
+//           (da = (dy . W2[e]^T) * act'(a):  X = dy, B = W2[e] = [F][H], K = H;
+//            dxe = da . W1[e]^T:            X = da, B = W1[e] = [H][F], K = F)
+//   wgrad   C[e][i][j] = sum_r P[r][i] Q[r][j]       both operands row-major over r
+//           (dW2[e] = h^T dy:  P = h, Q = dy;  dW1[e] = xp^T da:  P = xp, Q = da)
+//
+// The tile machinery is the forward's: 256 x 256 output tiles, 4 waves of
+// 128 x 128 on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, operands moved
+// HBM -> LDS by buffer_load ... lds through 4 stages of a 32-deep k-tile.  An
+// operand is either K-contiguous ("row" layout: LDS [idx][k], 64-byte rows,
+// plain 16-byte fragment reads) or row-major over k ("k-major": LDS [k][idx],
+// 512-byte rows, ds_read_b64_tr_b16 transposed fragment reads).  dgrad uses
+// row/row, wgrad k-major/k-major.  The MFMA's first operand is the side whose
+// index runs along the output row, so every lane owns 4 consecutive output
+// columns of one output row.  Out-of-range rows, columns and k read as zero
+// through the buffer resources' ranges or an out-of-range offset.
+#include "moe_internal.h"
+#include "lds_dma.h"
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kT = 256;                 // tile edge (both output dimensions)
+constexpr int kBK = 32;                 // k-tile depth
+constexpr int kNS = 4;                  // LDS stages
+constexpr int kOpBytes = kT * kBK * 2;  // one operand tile per stage: 16 KB
+constexpr int kStage = 2 * kOpBytes;
+constexpr int kLds = kNS * kStage;      // 128 KB
+constexpr int kF = 4;                   // 32 x 32 MFMA tiles per wave and dimension
+constexpr int kDmaPerOp = kOpBytes / 4096;   // 1 KB DMA blocks per wave per operand
+
+enum Layout { kRow = 0, kKmaj = 1 };
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
+// One operand of a tile: a buffer resource whose byte 0 is element (idx0, k0)
+// of the tile's block, the row stride in bytes, the number of valid indices
+// (along the tile edge) and of valid k.
+struct Operand {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t ld;        // bytes between consecutive rows of the source
+    int n_idx;          // valid indices from idx0 (rows for kRow, columns for kKmaj)
+    int n_k;            // valid k from k0
+};
+
+// Byte offset (within the operand's resource) of DMA q's 16 bytes for k-tile
+// t, and the LDS byte offset it lands at, for this lane.
+template <int L>
+__device__ __forceinline__ uint32_t dma_src(const Operand& o, int q, int t) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = 4 * q + wave;                       // 1 KB block of the stage tile
+    if constexpr (L == kRow) {
+        // 16 rows of 64 bytes per block; chunk c of row idx stored at c ^ ((idx >> 2) & 3)
+        const int idx = 16 * blk + (lane >> 2);
+        const int c = (lane & 3) ^ ((idx >> 2) & 3);
+        const int k = t * kBK + 8 * c;
+        if (idx >= o.n_idx || k >= o.n_k) return kOob;
+        return (uint32_t)idx * o.ld + (uint32_t)k * 2u;
+    } else {
+        // 2 rows of 512 bytes per block; chunk c of row k stored at c ^ (4 (k & 3))
+        const int kr = 2 * blk + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * (kr & 3));
+        const int k = t * kBK + kr;
+        if (8 * c >= o.n_idx || k >= o.n_k) return kOob;
+        return (uint32_t)k * o.ld + (uint32_t)(8 * c) * 2u;
+    }
+}
+
+// LDS byte offset (relative to the operand's tile in a stage) of fragment f of
+// the wave's 128-wide half `w0` for k-substep kk; kRow returns one 16-byte
+// read, kKmaj the first of two 8-byte transposed reads (the second is 4 rows on).
+template <int L>
+__device__ __forceinline__ uint32_t frag_addr(int w0, int f, int kk) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (L == kRow) {
+        const int idx = w0 + 32 * f + (lane & 31);
+        const int pc = (2 * kk + (lane >> 5)) ^ ((idx >> 2) & 3);
+        return (uint32_t)(idx * kBK * 2 + pc * 16);
+    } else {
+        const int grp = lane >> 4, s16 = lane & 15;
+        const int k = 8 * (grp >> 1) + (s16 >> 2);
+        const int idx = w0 + 32 * f + 16 * (grp & 1) + 4 * (s16 & 3);
+        const int pc = (idx >> 3) ^ (4 * (k & 3));
+        return (uint32_t)((k + 16 * kk) * 512 + pc * 16 + (idx & 4) * 2);
+    }
+}
+
+template <int L>
+__device__ __forceinline__ bf16x8_t read_frag(uint32_t a) {
+    if constexpr (L == kRow) {
+        return *(const lds_bf16x8_t*)(uintptr_t)a;
+    } else {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)a);
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)(a + 4 * 512));
+        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8_t, v);
+    }
+}
+
+// acc[i][j] += A-side fragments i (wave column half) x B-side fragments j
+// (wave row half) over nk k-tiles.  A: first MFMA operand (output columns),
+// B: second (output rows).
+template <int LA, int LB>
+__device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B, int nk,
+                                             char* lds, f32x16_t (&acc)[kF][kF]) {
+    const int wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    constexpr int NDMA = 2 * kDmaPerOp;
+    auto issue_one = [&](int t, int q) {
+        const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
+        const int wave_ = threadIdx.x >> 6;
+        if (q < kDmaPerOp) {
+            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave_) * 1024));
+            dma16(A.rsrc, dma_src<LA>(A, q, t), l);
+        } else {
+            const int qb = q - kDmaPerOp;
+            const uint32_t l = __builtin_amdgcn_readfirstlane(
+                st + (uint32_t)(kOpBytes + (4 * qb + wave_) * 1024));
+            dma16(B.rsrc, dma_src<LB>(B, qb, t), l);
+        }
+    };
+    bf16x8_t fa[2][kF], fb[2][kF];
+    auto read_frags = [&](int t, int kk, int buf) {
+        const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
+#pragma unroll
+        for (int f = 0; f < kF; ++f) fa[buf][f] = read_frag<LA>(st + frag_addr<LA>(128 * wn, f, kk));
+#pragma unroll
+        for (int f = 0; f < kF; ++f)
+            fb[buf][f] = read_frag<LB>(st + kOpBytes + frag_addr<LB>(128 * wm, f, kk));
+    };
+    auto mfma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kF; ++i)
+#pragma unroll
+            for (int j = 0; j < kF; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
+                                                                    acc[i][j], 0, 0, 0);
+    };
+
+    // DMA runs NS-1 k-tiles ahead: half of a k-tile's DMAs are issued after the
+    // barrier that frees their stage, the other half during the next substep.
+    constexpr int H1 = NDMA / 2, H2 = NDMA - H1;
+#pragma unroll
+    for (int t = 0; t + 1 < kNS; ++t)
+#pragma unroll
+        for (int q = 0; q < NDMA; ++q) issue_one(t, q);
+#pragma unroll
+    for (int q = 0; q < H1; ++q) issue_one(kNS - 1, q);
+    wait_vmcnt<(kNS - 2) * NDMA + H1>();
+    lds_barrier();
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        // substep 0 MFMAs, substep 1 fragments, the rest of k-tile kt+NS-1's DMAs
+#pragma unroll
+        for (int q = 0; q < H2; ++q) issue_one(kt + kNS - 1, H1 + q);
+        read_frags(kt, 1, 1);
+        mfma(0);
+        // k-tile kt+1 has landed for every wave; stage kt % NS is free again
+        wait_vmcnt<(kNS - 2) * NDMA>();
+        wait_lgkm0();
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < H1; ++q) issue_one(kt + kNS, q);
+        read_frags(kt + 1, 0, 0);
+        mfma(1);
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+}
+
+__device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
+#pragma unroll
+    for (int i = 0; i < kF; ++i)
+#pragma unroll
+        for (int j = 0; j < kF; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// ---------------------------------------------------------------- dgrad
+// Workgroup p: row tile p / Nt (over the experts' kept rows, 256 rows each,
+// never straddling experts) x column tile p % Nt.  EPI_DA: multiply by
+// act'(pre[r][n]); EPI_PLAIN: store as is.  Output bf16 [rows][N].
+enum { kEpiPlain = 0, kEpiDa = 1 };
+
+template <int EPI, int ACT>
+__global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
+                                                 const int32_t* __restrict__ offsets, int E,
+                                                 const uint16_t* __restrict__ Bw,
+                                                 const uint16_t* __restrict__ pre,
+                                                 uint16_t* __restrict__ C, int K, int N, int Nt) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    const int p = blockIdx.x;
+    const int mt = p / Nt, nt = p % Nt;
+    int e, m0, row_begin, n_rows;
+    if (!find_tile<kT>(offsets, E, mt, e, m0, row_begin, n_rows)) return;
+    const int n0 = nt * kT;
+    const int rows = min(kT, n_rows - m0);
+    Operand a, b;
+    // A (output columns): B[e][n0 ..][k], K-contiguous rows of the expert's weights
+    a.rsrc = make_rsrc(uniform_ptr(Bw + ((int64_t)e * N + n0) * K), (uint32_t)min(kT, N - n0) * K * 2u);
+    a.ld = (uint32_t)K * 2u;
+    a.n_idx = min(kT, N - n0);
+    a.n_k = K;
+    // B (output rows): X[row_begin + m0 ..][k]
+    b.rsrc = make_rsrc(uniform_ptr(X + (int64_t)(row_begin + m0) * K), (uint32_t)rows * K * 2u);
+    b.ld = (uint32_t)K * 2u;
+    b.n_idx = rows;
+    b.n_k = K;
+    f32x16_t acc[kF][kF];
+    zero(acc);
+    bwd_mainloop<kRow, kRow>(a, b, (K + kBK - 1) / kBK, lds, acc);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < kF; ++j) {
+        const int m = 128 * wm + 32 * j + l32;
+        if (m >= rows) continue;
+        const int64_t row = (int64_t)(row_begin + m0 + m) * N;
+#pragma unroll
+        for (int i = 0; i < kF; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + 128 * wn + 32 * i + 8 * g + 4 * half;
+                if (n >= N) continue;                       // N % 8 == 0: all 4 columns valid
+                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+                if constexpr (EPI == kEpiDa) {
+                    const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(pre + row + n);
+                    v[0] *= activate_grad<ACT>(bf16_lo(pa[0]));
+                    v[1] *= activate_grad<ACT>(bf16_hi(pa[0]));
+                    v[2] *= activate_grad<ACT>(bf16_lo(pa[1]));
+                    v[3] *= activate_grad<ACT>(bf16_hi(pa[1]));
+                }
+                u32x2_t o;
+                o[0] = pack_bf16x2(v[0], v[1]);
+                o[1] = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<u32x2_t*>(C + row + n) = o;
+            }
+    }
+}
+
+// ---------------------------------------------------------------- wgrad
+// Workgroup p: expert p / (It Jt), output tile (i, j) of C[e] [I][J] (fp32):
+// C[e][i][j] = sum over the expert's rows r of P[r][i] Q[r][j].  An expert
+// without rows gets zeros.
+__global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
+                                                 const uint16_t* __restrict__ Q,
+                                                 const int32_t* __restrict__ offsets, int I,
+                                                 int J, int It, int Jt, float* __restrict__ C) {
+    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    const int p = blockIdx.x;
+    const int e = p / (It * Jt), ij = p % (It * Jt);
+    const int i0 = (ij / Jt) * kT, j0 = (ij % Jt) * kT;
+    const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+    const int nr = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - r0;
+    Operand a, b;
+    // A (output columns j): Q[r0 + k][j0 ..]
+    a.rsrc = make_rsrc(uniform_ptr(Q + (int64_t)r0 * J + j0), (uint32_t)nr * J * 2u);
+    a.ld = (uint32_t)J * 2u;
+    a.n_idx = min(kT, J - j0);
+    a.n_k = nr;
+    // B (output rows i): P[r0 + k][i0 ..]
+    b.rsrc = make_rsrc(uniform_ptr(P + (int64_t)r0 * I + i0), (uint32_t)nr * I * 2u);
+    b.ld = (uint32_t)I * 2u;
+    b.n_idx = min(kT, I - i0);
+    b.n_k = nr;
+    f32x16_t acc[kF][kF];
+    zero(acc);
+    bwd_mainloop<kKmaj, kKmaj>(a, b, (nr + kBK - 1) / kBK, lds, acc);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int l32 = lane & 31, half = lane >> 5;
+    float* Ce = C + (int64_t)e * I * J;
+#pragma unroll
+    for (int jj = 0; jj < kF; ++jj) {
+        const int i = i0 + 128 * wm + 32 * jj + l32;
+        if (i >= I) continue;
+#pragma unroll
+        for (int ii = 0; ii < kF; ++ii)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int j = j0 + 128 * wn + 32 * ii + 8 * g + 4 * half;
+                if (j >= J) continue;
+                const f32x4_t v = {acc[ii][jj][4 * g], acc[ii][jj][4 * g + 1],
+                                   acc[ii][jj][4 * g + 2], acc[ii][jj][4 * g + 3]};
+                *reinterpret_cast<f32x4_t*>(Ce + (int64_t)i * J + j) = v;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, const int32_t* offsets,
+                            const void* Bw, const void* pre, void* C, int K, int N,
+                            hipStream_t s) {
+    const int64_t rows = p.T * p.k;
+    const int Mt = (int)((rows + kT - 1) / kT + p.E);          // row tiles, worst case
+    const int Nt = (N + kT - 1) / kT;
+    const dim3 grid((unsigned)((int64_t)Mt * Nt)), block(256);
+    auto* x = static_cast<const uint16_t*>(X);
+    auto* b = static_cast<const uint16_t*>(Bw);
+    auto* pr = static_cast<const uint16_t*>(pre);
+    auto* c = static_cast<uint16_t*>(C);
+    if (!da)
+        bwd_dgrad<kEpiPlain, kActNone><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+    else if (p.activation == MOE_ACT_SILU)
+        bwd_dgrad<kEpiDa, kActSilu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+    else
+        bwd_dgrad<kEpiDa, kActGelu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad(const moe_problem_t& p, const void* P, const void* Q,
+                            const int32_t* offsets, int I, int J, float* C, hipStream_t s) {
+    const int It = (I + kT - 1) / kT, Jt = (J + kT - 1) / kT;
+    bwd_wgrad<<<dim3((unsigned)(p.E * It * Jt)), dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(Q), offsets, I, J, It, Jt, C);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -261,4 +261,12 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
     return hipGetLastError();
 }
 
+hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* pos, void* xp,
+                         hipStream_t s) {
+    const int64_t row_bytes = (int64_t)p.H * (p.dtype == MOE_DTYPE_BF16 ? 2 : 4);
+    gather_tokens<<<dim3((unsigned)p.T), dim3(kGatherThreads), 0, s>>>(
+        static_cast<const u32x4_t*>(x), pos, p.k, row_bytes / 16, static_cast<u32x4_t*>(xp));
+    return hipGetLastError();
+}
+
 }  // namespace moe

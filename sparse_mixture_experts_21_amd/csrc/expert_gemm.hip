@@ -32,92 +32,10 @@
 // the epilogue (bias, activation, bf16).
 #include "moe_internal.h"
 #include "lds_dma.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
-
-enum Act { kActNone = 0, kActGelu = 1, kActSilu = 2 };
-
-// Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)) = max(a, 0) - 0.5 |a| q with
-// q = 1 - erf(|a| / sqrt 2) (erf is odd; no cancellation for a < 0, where the
-// result is the small 0.5 a q), erf evaluated by formula 7.1.26 of Abramowitz & Stegun,
-// Handbook of Mathematical Functions:
-//   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
-//   t = 1 / (1 + p u), u >= 0, |error| <= 1.5e-7,
-// i.e. below fp32 rounding of GELU's output scale and far below bf16.  With
-// u = |a| / sqrt 2 the factor 1/sqrt 2 folds into p, and exp(-u^2) is
-// 2^(a^2 * (-1 / (2 ln 2))).  One reciprocal and one exponential, no branches.
-__device__ __forceinline__ float gelu_erf(float a) {
-    const float aa = fabsf(a);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
-    const float q = t * poly * ex;                        // 1 - erf(|a| / sqrt 2)
-    return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
-}
-
-// SiLU, a * sigmoid(a) = a / (1 + e^-a) with e^-a = 2^(-a log2 e).  For very
-// negative a the denominator overflows to +inf and the result is -0; for very
-// positive a it is 1 and the result is a.
-__device__ __forceinline__ float silu(float a) {
-    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
-}
-
-template <int ACT>
-__device__ __forceinline__ float activate(float v) {
-    if constexpr (ACT == kActGelu) return gelu_erf(v);
-    else if constexpr (ACT == kActSilu) return silu(v);
-    else return v;
-}
-
-// Locate the expert and row tile of row-tile index mt.  Returns false when mt
-// is beyond the last real tile.  The whole wave walks 64 experts at a time
-// (tile counts, a shuffle scan, a ballot), so the cost grows with E / 64.
-template <int BM>
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt,
-                                          int& e_out, int& m0, int& row_begin, int& n_rows) {
-    const int lane = threadIdx.x & 63;
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        const int b = e < E ? offsets[e] : 0;
-        const int n = e < E ? offsets[e + 1] - b : 0;
-        const int tiles = (n + BM - 1) / BM;
-        int incl = tiles;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int t = __shfl_up(incl, d);
-            if (lane >= d) incl += t;
-        }
-        const int excl = incl - tiles;
-        const uint64_t hit = __ballot(e < E && mt >= base + excl && mt < base + incl);
-        if (hit) {
-            // wave-uniform results, pinned to scalar registers
-            const int src = __ffsll((unsigned long long)hit) - 1;
-            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src));
-            m0 = __builtin_amdgcn_readfirstlane((mt - base - __shfl(excl, src)) * BM);
-            row_begin = __builtin_amdgcn_readfirstlane(__shfl(b, src));
-            n_rows = __builtin_amdgcn_readfirstlane(__shfl(n, src));
-            return true;
-        }
-        base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-    }
-    return false;
-}
-
-// Real row tiles over all experts (every lane gets the same value).
-template <int BM>
-__device__ __forceinline__ int real_row_tiles(const int32_t* __restrict__ offsets, int E) {
-    const int lane = threadIdx.x & 63;
-    int t = 0;
-    for (int e = lane; e < E; e += 64) t += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
-    return t;
-}
 
 // ---------------------------------------------------------------- bf16 MFMA
 #ifndef MOE_GEMM_BK
@@ -466,24 +384,18 @@ __device__ __forceinline__ void gemm_mainloop(
 }
 
 // Bias, activation, bf16 and the store of tile `tr` from the accumulators.
-template <int BM, int ACT>
-__device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
+// One pass of the epilogue: bias and activation A (kActNone: the
+// pre-activation itself) in fp32, one rounding to bf16, the tile staged in LDS
+// and written to out as full rows.  The caller has passed an LDS barrier.
+template <int BM, int A>
+__device__ __forceinline__ void epilogue_pass(const TileRef& tr,
                                               f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
-                                              char* lds, const uint16_t* __restrict__ bias,
-                                              uint16_t* __restrict__ C, int N) {
+                                              char* lds, const uint16_t* __restrict__ be,
+                                              uint16_t* __restrict__ out, int N) {
     using G = Cfg<BM>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
     const int l32 = lane & 31, half = lane >> 5;
-    // ---- epilogue.  D[n][m]: a lane owns m = l32 and n = 8 g + 4 half + 0..3 of
-    // each 32x32 tile.  Bias and activation in fp32, one rounding to bf16, then
-    // the whole output tile is staged in LDS ([m][n], 528-byte pitch: the
-    // 8-byte writes of 16 consecutive rows and the 16-byte reads of one row are
-    // both bank-conflict free) and written out as full contiguous row
-    // segments, so every 128-byte line of the output is written once.
-    wait_lgkm0();
-    lds_barrier();
-    const uint16_t* be = bias ? bias + (int64_t)tr.e * N : nullptr;
 #pragma unroll
     for (int i = 0; i < G::FN; ++i) {
 #pragma unroll
@@ -504,7 +416,7 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
                 float v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    v[q] = activate<ACT>(acc[i][j][4 * g + q] + bv[q]);
+                    v[q] = activate<A>(acc[i][j][4 * g + q] + bv[q]);
                 }
                 u32x2_t o;
                 o[0] = pack_bf16x2(v[0], v[1]);
@@ -516,13 +428,36 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
     lds_barrier();
     const int rows = min(G::BM_ROWS, tr.n_rows - tr.m0);
     const int chunks = min(G::BN, N - tr.n0) / 8;         // 16-byte chunks per row (N % 8 == 0)
-    uint16_t* cbase = C + (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
+    uint16_t* cbase = out + (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
     for (int idx = tid; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
         const int r = idx / (G::BN / 8), c = idx % (G::BN / 8);
         if (r < rows && c < chunks)
             *reinterpret_cast<u32x4_t*>(cbase + (int64_t)r * N + c * 8) =
                 *reinterpret_cast<const u32x4_t*>(lds + r * G::OP + c * 16);
     }
+}
+
+// Bias, activation, bf16 and the store of tile `tr` from the accumulators.
+// D[n][m]: a lane owns m = l32 and n = 8 g + 4 half + 0..3 of each 32x32 tile.
+// The tile is staged in LDS ([m][n], 528-byte pitch: the 8-byte writes of 16
+// consecutive rows and the 16-byte reads of one row are both bank-conflict
+// free) and written out as full contiguous row segments, so every 128-byte
+// line of the output is written once.  SAVE: the pre-activation (with bias) is
+// first written to Cpre the same way (kept for the backward).
+template <int BM, int ACT, bool SAVE>
+__device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
+                                              f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
+                                              char* lds, const uint16_t* __restrict__ bias,
+                                              uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
+                                              int N) {
+    wait_lgkm0();
+    lds_barrier();
+    const uint16_t* be = bias ? bias + (int64_t)tr.e * N : nullptr;
+    if constexpr (SAVE) {
+        epilogue_pass<BM, kActNone>(tr, acc, lds, be, Cpre, N);
+        lds_barrier();
+    }
+    epilogue_pass<BM, ACT>(tr, acc, lds, be, C, N);
 }
 
 // fp32 partial tile of one K slice, row-major [BM][BN] (Cfg<BM>::UNIT floats
@@ -570,17 +505,18 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
 }
 
 // One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
-template <int TB, int ACT, bool NTW>
+template <int TB, int ACT, bool NTW, bool SAVE>
 __device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
                                            const uint16_t* __restrict__ X, uint32_t x_bytes,
                                            const int32_t* __restrict__ rowmap,
                                            const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ bias,
-                                           uint16_t* __restrict__ C, int K, int N) {
+                                           uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
+                                           int K, int N) {
     f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
     zero_acc<TB>(acc);
     gemm_mainloop<TB, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
-    gemm_epilogue<TB, ACT>(tr, acc, lds, bias, C, N);
+    gemm_epilogue<TB, ACT, SAVE>(tr, acc, lds, bias, C, Cpre, N);
 }
 
 // Workgroup p: whole tile p (p < full), or one K slice of a tail tile.  `part`
@@ -588,12 +524,12 @@ __device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
 // row tile of an expert is usually short: with at most 128 (64) real rows it
 // runs the 128-row (64-row) layout, whose four waves split the columns instead
 // of idling on rows that do not exist.
-template <int BM, int ACT>
+template <int BM, int ACT, bool SAVE>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, int K, int N, int Nt, int SBN,
-    int ncu, float* __restrict__ part) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
+    int K, int N, int Nt, int SBN, int ncu, float* __restrict__ part) {
     using G = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
     // With at most 128 rows per tile (few rows per expert) an expert's weights
@@ -622,17 +558,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         const int rows = tr.n_rows - tr.m0;
         if constexpr (BM >= 128) {
             if (rows <= 64) {
-                whole_tile<64, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                whole_tile<64, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                                                  N);
                 return;
             }
         }
         if constexpr (BM >= 256) {
             if (rows <= 128) {
-                whole_tile<128, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+                whole_tile<128, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                                                   N);
                 return;
             }
         }
-        whole_tile<BM, ACT, kNtW>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, K, N);
+        whole_tile<BM, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
         return;
     }
     f32x16_t acc[G::FN][G::FM];
@@ -656,7 +594,7 @@ struct FixCfg {
 template <int BM, int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ C, int K, int N, int Nt, int SBN, int ncu,
+    uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre, int K, int N, int Nt, int SBN, int ncu,
     const float* __restrict__ part) {
     using G = Cfg<BM>;
     const int nk = (K + G::BK - 1) / G::BK;
@@ -699,11 +637,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
         }
         float o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(a[q] + bv[q]);
+        for (int q = 0; q < 4; ++q) o[q] = a[q] + bv[q];
+        const int64_t at = (int64_t)(tr.row_begin + tr.m0 + r) * N + tr.n0 + col;
         u32x2_t w;
+        if (Cpre) {                                       // pre-activation kept for the backward
+            w[0] = pack_bf16x2(o[0], o[1]);
+            w[1] = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<u32x2_t*>(Cpre + at) = w;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(o[q]);
         w[0] = pack_bf16x2(o[0], o[1]);
         w[1] = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<u32x2_t*>(C + (int64_t)(tr.row_begin + tr.m0 + r) * N + tr.n0 + col) = w;
+        *reinterpret_cast<u32x2_t*>(C + at) = w;
     }
 }
 
@@ -808,25 +754,30 @@ int gemm_nt(int N) { return (N + 255) / 256; }
 // most half a round of tail tiles (each is cut in 2 or more).
 template <int BM, int ACT>
 hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
-                 int E, const uint16_t* w, const uint16_t* b, uint16_t* c, int K, int N, int Mt,
-                 int Nt, int SBN, int ncu, float* part, hipEvent_t mid, hipStream_t s) {
+                 int E, const uint16_t* w, const uint16_t* b, uint16_t* c, uint16_t* cpre, int K,
+                 int N, int Mt, int Nt, int SBN, int ncu, float* part, hipEvent_t mid,
+                 hipStream_t s) {
     const int units = std::min(ncu, kMaxUnits);
-    const dim3 block(256);
-    ffn_gemm_bf16<BM, ACT><<<dim3((unsigned)((int64_t)Mt * Nt + units)), block, 0, s>>>(
-        x, xb, rowmap, offsets, E, w, b, c, K, N, Nt, SBN, ncu, part);
+    const dim3 block(256), grid((unsigned)((int64_t)Mt * Nt + units));
+    if (cpre)
+        ffn_gemm_bf16<BM, ACT, true><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b, c,
+                                                            cpre, K, N, Nt, SBN, ncu, part);
+    else
+        ffn_gemm_bf16<BM, ACT, false><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b, c,
+                                                             nullptr, K, N, Nt, SBN, ncu, part);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
     if (part)
         ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
-            offsets, E, b, c, K, N, Nt, SBN, ncu, part);
+            offsets, E, b, c, cpre, K, N, Nt, SBN, ncu, part);
     return hipGetLastError();
 }
 
 template <int ACT>
 hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* rowmap,
                        const int32_t* offsets, const void* W, const void* bias, void* Cout,
-                       int K, int N, float* part, hipEvent_t mid, hipStream_t s) {
+                       void* Cpre, int K, int N, float* part, hipEvent_t mid, hipStream_t s) {
     const int64_t rows = p.T * p.k;
     if (p.dtype == MOE_DTYPE_BF16) {
         const int bm = pick_bm(p);
@@ -839,18 +790,19 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         auto* w = static_cast<const uint16_t*>(W);
         auto* b = static_cast<const uint16_t*>(bias);
         auto* c = static_cast<uint16_t*>(Cout);
+        auto* cp = static_cast<uint16_t*>(Cpre);
         // bytes addressable through X: the token rows (gather) or the kept rows
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
         hipError_t e;
         if (bm == 256)
-            e = launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+            e = launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
                                   mid, s);
         else if (bm == 128)
-            e = launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+            e = launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
                                   mid, s);
         else
-            e = launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, K, N, Mt, Nt, SBN, ncu, part,
+            e = launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
                                  mid, s);
         return e;
     } else {
@@ -868,16 +820,19 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
 
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         float* part, hipEvent_t mid, hipStream_t s) {
+                         void* hpre, float* part, hipEvent_t mid, hipStream_t s) {
     if (p.activation == MOE_ACT_SILU)
-        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, mid, s);
-    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, p.H, p.F, part, mid, s);
+        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, hpre, p.H, p.F, part,
+                                     mid, s);
+    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, hpre, p.H, p.F, part, mid,
+                                 s);
 }
 
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
                            hipStream_t s) {
-    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, p.F, p.H, part, mid, s);
+    return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, nullptr, p.F, p.H, part, mid,
+                                 s);
 }
 
 size_t gemm_partial_bytes(const moe_problem_t& p) {

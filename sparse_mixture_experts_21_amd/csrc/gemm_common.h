@@ -1,0 +1,122 @@
+// Device helpers shared by the grouped GEMM kernels of the forward and the
+// backward: the expert activations and their derivatives, and the lookup of
+// an expert's row tile from the row offsets.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+enum Act { kActNone = 0, kActGelu = 1, kActSilu = 2 };
+
+// Exact (erf) GELU, 0.5 a (1 + erf(a / sqrt 2)) = max(a, 0) - 0.5 |a| q with
+// q = 1 - erf(|a| / sqrt 2) (erf is odd; no cancellation for a < 0, where the
+// result is the small 0.5 a q), erf evaluated by formula 7.1.26 of Abramowitz & Stegun,
+// Handbook of Mathematical Functions:
+//   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
+//   t = 1 / (1 + p u), u >= 0, |error| <= 1.5e-7,
+// i.e. below fp32 rounding of GELU's output scale and far below bf16.  With
+// u = |a| / sqrt 2 the factor 1/sqrt 2 folds into p, and exp(-u^2) is
+// 2^(a^2 * (-1 / (2 ln 2))).  One reciprocal and one exponential, no branches.
+__device__ __forceinline__ float gelu_erf(float a) {
+    const float aa = fabsf(a);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
+    const float q = t * poly * ex;                        // 1 - erf(|a| / sqrt 2)
+    return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
+}
+
+// SiLU, a * sigmoid(a) = a / (1 + e^-a) with e^-a = 2^(-a log2 e).  For very
+// negative a the denominator overflows to +inf and the result is -0; for very
+// positive a it is 1 and the result is a.
+__device__ __forceinline__ float silu(float a) {
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+    if constexpr (ACT == kActGelu) return gelu_erf(v);
+    else if constexpr (ACT == kActSilu) return silu(v);
+    else return v;
+}
+
+// Locate the expert and row tile of row-tile index mt.  Returns false when mt
+// is beyond the last real tile.  The whole wave walks 64 experts at a time
+// (tile counts, a shuffle scan, a ballot), so the cost grows with E / 64.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int mt,
+                                          int& e_out, int& m0, int& row_begin, int& n_rows) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int b = e < E ? offsets[e] : 0;
+        const int n = e < E ? offsets[e + 1] - b : 0;
+        const int tiles = (n + BM - 1) / BM;
+        int incl = tiles;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d);
+            if (lane >= d) incl += t;
+        }
+        const int excl = incl - tiles;
+        const uint64_t hit = __ballot(e < E && mt >= base + excl && mt < base + incl);
+        if (hit) {
+            // wave-uniform results, pinned to scalar registers
+            const int src = __ffsll((unsigned long long)hit) - 1;
+            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, src));
+            m0 = __builtin_amdgcn_readfirstlane((mt - base - __shfl(excl, src)) * BM);
+            row_begin = __builtin_amdgcn_readfirstlane(__shfl(b, src));
+            n_rows = __builtin_amdgcn_readfirstlane(__shfl(n, src));
+            return true;
+        }
+        base += __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    }
+    return false;
+}
+
+// Real row tiles over all experts (every lane gets the same value).
+template <int BM>
+__device__ __forceinline__ int real_row_tiles(const int32_t* __restrict__ offsets, int E) {
+    const int lane = threadIdx.x & 63;
+    int t = 0;
+    for (int e = lane; e < E; e += 64) t += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+    return t;
+}
+
+// Derivatives for the backward.  GELU'(a) = Phi(a) + a phi(a): with q as in
+// gelu_erf, Phi(a) = 1 - q/2 for a >= 0 and q/2 below, and phi(a) =
+// exp(-a^2 / 2) / sqrt(2 pi) is the same exponential times 1 / sqrt(2 pi).
+__device__ __forceinline__ float gelu_erf_grad(float a) {
+    const float aa = fabsf(a);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
+    const float q = t * poly * ex;
+    const float Phi = a >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+    return fmaf(a * 0.39894228040143267794f, ex, Phi);
+}
+
+// SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a) (0 for very negative a).
+__device__ __forceinline__ float silu_grad(float a) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
+    return s * fmaf(a, 1.0f - s, 1.0f);
+}
+
+template <int ACT>
+__device__ __forceinline__ float activate_grad(float v) {
+    if constexpr (ACT == kActGelu) return gelu_erf_grad(v);
+    else if constexpr (ACT == kActSilu) return silu_grad(v);
+    else return 1.0f;
+}
+
+}  // namespace moe

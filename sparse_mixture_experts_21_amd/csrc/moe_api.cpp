@@ -164,6 +164,95 @@ int64_t capacity_of(const moe_problem_t& p) {
     return (int64_t)c;
 }
 
+// ---------------------------------------------------------------- training
+// Workspace of moe_forward_train / moe_backward: the forward's layout (whose
+// routing, dispatch, h and y the backward reads) followed by the fp32
+// logits, the pre-activation rows a, and the backward's scratch: dy, dl, da,
+// dxe (the expert part of dx per kept row), the gathered rows xp and the
+// partial sums of the gate gradients.
+struct TrainLayout {
+    WsLayout L;
+    size_t logits, a, dy, dl, da, dxe, xp, gpart, gpb, total;
+};
+
+TrainLayout train_layout(const moe_problem_t& p) {
+    TrainLayout X;
+    X.L = ws_layout(p);
+    const size_t T = (size_t)p.T, H = (size_t)p.H, E = (size_t)p.E, k = (size_t)p.k,
+                 F = (size_t)p.F;
+    const size_t nc = (size_t)bwd_gate_chunks(p);
+    size_t off = X.L.total;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    X.logits = take(T * E * 4);
+    X.a = take(T * k * F * 2);
+    X.dy = take(T * k * H * 2);
+    X.dl = take(T * E * 4);
+    X.da = take(T * k * F * 2);
+    X.dxe = take(T * k * H * 2);
+    X.xp = take(T * k * H * 2);
+    X.gpart = take(nc * H * E * 4);
+    X.gpb = take(nc * E * 4);
+    X.total = off;
+    return X;
+}
+
+// The backward runs on bf16 storage; its weight-gradient GEMMs address one
+// expert's rows of h, dy, xp and da through 32-bit buffer offsets.
+moe_status_t check_train(const moe_problem_t* p) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (p->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->T * p->k * (int64_t)std::max(p->H, p->F) * 2 >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// The forward's launch sequence; NULL outputs live in the workspace.  hpre
+// (nullable): also keep the first GEMM's pre-activation rows.
+moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, const void* x,
+                          const void* Wg, const void* bg, const void* W1, const void* b1,
+                          const void* W2, const void* b2, void* out, float* losses,
+                          float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                          int32_t* offsets, int32_t* pos, void* hpre, hipStream_t stream,
+                          hipEvent_t* stage_events) {
+    const moe_problem_t* p = &P;
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + L.topk_idx);
+    float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.topk_w);
+    int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(w + L.counts);
+    int32_t* off = offsets ? offsets : reinterpret_cast<int32_t*>(w + L.offsets);
+    int32_t* ps = pos ? pos : reinterpret_cast<int32_t*>(w + L.pos);
+    int32_t* rt = reinterpret_cast<int32_t*>(w + L.row_token);
+    void* h = w + L.h;
+    void* y = w + L.y;
+
+    auto ev = [&](int i) -> hipError_t {
+        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+    };
+    hipError_t e = ev(MOE_EV_ROUTE);
+    if (e == hipSuccess)
+        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, false,
+                         stream);
+    if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
+    if (e == hipSuccess)
+        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt, losses,
+                           stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
+    float* part = reinterpret_cast<float*>(w + L.gemm_part);
+    hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
+    hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
+    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, hpre, part, up_fix, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
+    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
+    if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
+    if (e == hipSuccess) e = ev(MOE_EV_END);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,7 +334,7 @@ moe_status_t moe_expert_ffn(const moe_problem_t* p, const void* xp, const int32_
     // is cut along K (see moe_workspace_bytes)
     float* part = (ws && aligned16(ws) && ws_bytes >= gemm_partial_bytes(*p))
                       ? static_cast<float*>(ws) : nullptr;
-    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, part, nullptr, stream);
+    hipError_t e = launch_ffn_up(*p, xp, nullptr, offsets, W1, b1, h, nullptr, part, nullptr, stream);
     if (e == hipSuccess) e = launch_ffn_down(*p, h, offsets, W2, b2, y, part, nullptr, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -281,38 +370,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
         return MOE_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(*p);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    char* w = static_cast<char*>(ws);
-    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + L.topk_idx);
-    float* tw = topk_w ? topk_w : reinterpret_cast<float*>(w + L.topk_w);
-    int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(w + L.counts);
-    int32_t* off = offsets ? offsets : reinterpret_cast<int32_t*>(w + L.offsets);
-    int32_t* ps = pos ? pos : reinterpret_cast<int32_t*>(w + L.pos);
-    int32_t* rt = reinterpret_cast<int32_t*>(w + L.row_token);
-    void* h = w + L.h;
-    void* y = w + L.y;
-
-    auto ev = [&](int i) -> hipError_t {
-        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
-    };
-    hipError_t e = ev(MOE_EV_ROUTE);
-    if (e == hipSuccess)
-        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, false,
-                         stream);
-    if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
-    if (e == hipSuccess)
-        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt, losses,
-                           stream);
-    if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
-    float* part = reinterpret_cast<float*>(w + L.gemm_part);
-    hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
-    hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
-    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, part, up_fix, stream);
-    if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
-    if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
-    if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
-    if (e == hipSuccess) e = ev(MOE_EV_END);
-    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return forward_impl(*p, L, static_cast<char*>(ws), x, Wg, bg, W1, b1, W2, b2, out, losses,
+                        logits, topk_idx, topk_w, counts, offsets, pos, nullptr, stream,
+                        stage_events);
 }
 
 moe_status_t moe_ec_capacity(const moe_problem_t* p, int64_t group, int64_t* C) {
@@ -403,12 +463,86 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, co
     if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
     if (e == hipSuccess) e = launch_expert_choice(*p, group, X.C, lg, pr, sl, ro, off, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
-    if (e == hipSuccess) e = launch_ffn_up(X.pg, x, sl, off, W1, b1, h, part, up_fix, stream);
+    if (e == hipSuccess) e = launch_ffn_up(X.pg, x, sl, off, W1, b1, h, nullptr, part, up_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
     if (e == hipSuccess) e = launch_ffn_down(X.pg, h, off, W2, b2, y, part, down_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
     if (e == hipSuccess) e = launch_combine(pc, y, ro, pr, out, stream);
     if (e == hipSuccess) e = ev(MOE_EV_END);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_train_workspace_bytes(const moe_problem_t* p, size_t* bytes) {
+    moe_status_t st = check_train(p);
+    if (st != MOE_OK) return st;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = train_layout(*p).total;
+    return MOE_OK;
+}
+
+moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void* Wg,
+                               const void* bg, const void* W1, const void* b1, const void* W2,
+                               const void* b2, void* out, float* losses, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    moe_status_t st = check_train(p);
+    if (st != MOE_OK) return st;
+    if (!x || !Wg || !W1 || !W2 || !out || !losses || !ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
+        !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !aligned16(losses) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const TrainLayout X = train_layout(*p);
+    if (ws_bytes < X.total) return MOE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    return forward_impl(*p, X.L, w, x, Wg, bg, W1, b1, W2, b2, out, losses,
+                        reinterpret_cast<float*>(w + X.logits), nullptr, nullptr, nullptr,
+                        nullptr, nullptr, w + X.a, stream, nullptr);
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg, const void* W1,
+                          const void* W2, const void* dout, float g_aux, float g_z, void* dx,
+                          float* dWg, float* dbg, float* dW1, float* db1, float* dW2, float* db2,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    moe_status_t st = check_train(p);
+    if (st != MOE_OK) return st;
+    if (!x || !Wg || !W1 || !W2 || !dout || !dx || !dWg || !dW1 || !dW2 || !ws)
+        return MOE_ERR_INVALID_ARG;
+    if (std::isnan(g_aux) || std::isnan(g_z)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W2) || !aligned16(dout) ||
+        !aligned16(dx) || !aligned16(dWg) || !opt_ok(dbg) || !aligned16(dW1) || !opt_ok(db1) ||
+        !aligned16(dW2) || !opt_ok(db2) || !aligned16(ws))
+        return MOE_ERR_UNSUPPORTED;
+    const TrainLayout X = train_layout(*p);
+    if (ws_bytes < X.total) return MOE_ERR_WORKSPACE;
+    char* w = static_cast<char*>(ws);
+    const WsLayout& L = X.L;
+    auto* idx = reinterpret_cast<const int32_t*>(w + L.topk_idx);
+    auto* tw = reinterpret_cast<const float*>(w + L.topk_w);
+    auto* cnt = reinterpret_cast<const int32_t*>(w + L.counts);
+    auto* off = reinterpret_cast<const int32_t*>(w + L.offsets);
+    auto* ps = reinterpret_cast<const int32_t*>(w + L.pos);
+    auto* lg = reinterpret_cast<const float*>(w + X.logits);
+    float* dl = reinterpret_cast<float*>(w + X.dl);
+    void* dy = w + X.dy;
+    void* da = w + X.da;
+    void* dxe = w + X.dxe;
+    void* xp = w + X.xp;
+    const int H = p->H, F = p->F;
+
+    // dw, dy rows and the router's dl; then the two data-gradient GEMMs and dx
+    hipError_t e = launch_bwd_token(*p, dout, w + L.y, ps, idx, tw, lg, cnt, g_aux, g_z, dy, dl,
+                                    stream);
+    if (e == hipSuccess) e = launch_bwd_dgrad(*p, true, dy, off, W2, w + X.a, da, H, F, stream);
+    if (e == hipSuccess) e = launch_bwd_dgrad(*p, false, da, off, W1, nullptr, dxe, F, H, stream);
+    if (e == hipSuccess) e = launch_bwd_dx(*p, dxe, ps, dl, Wg, dx, stream);
+    // weight gradients
+    if (e == hipSuccess) e = launch_gather(*p, x, ps, xp, stream);
+    if (e == hipSuccess) e = launch_bwd_wgrad(*p, w + L.h, dy, off, F, H, dW2, stream);
+    if (e == hipSuccess) e = launch_bwd_wgrad(*p, xp, da, off, H, F, dW1, stream);
+    if (e == hipSuccess && db2) e = launch_bwd_colsum(*p, dy, off, H, db2, stream);
+    if (e == hipSuccess && db1) e = launch_bwd_colsum(*p, da, off, F, db1, stream);
+    if (e == hipSuccess)
+        e = launch_bwd_gate(*p, x, dl, reinterpret_cast<float*>(w + X.gpart),
+                            reinterpret_cast<float*>(w + X.gpb), dWg, dbg, stream);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -79,9 +79,10 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
 // part (nullable): fp32 buffer of gemm_partial_bytes(p) for the K slices of
 // the ragged last round of tiles; without it no tile is cut.
 // mid (nullable): event recorded between the GEMM launch and its fixup.
+// hpre (nullable, bf16 only): also store the pre-activation rows (with bias).
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         float* part, hipEvent_t mid, hipStream_t s);
+                         void* hpre, float* part, hipEvent_t mid, hipStream_t s);
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
                            hipStream_t s);
@@ -90,6 +91,27 @@ size_t gemm_partial_bytes(const moe_problem_t& p);
 // topk_w[t][s] * y[pos[t][s]]; any k (expert choice passes k = E).
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s);
+// ---- backward (bf16)
+hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* pos, void* xp,
+                         hipStream_t s);
+// dgrad: C[r][n] = sum_k X[r][k] Bw[e][n][k] over each expert's rows; da: times
+// act'(pre[r][n]).  wgrad: C[e][i][j] = sum over the rows of e of P[r][i] Q[r][j].
+hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, const int32_t* offsets,
+                            const void* Bw, const void* pre, void* C, int K, int N,
+                            hipStream_t s);
+hipError_t launch_bwd_wgrad(const moe_problem_t& p, const void* P, const void* Q,
+                            const int32_t* offsets, int I, int J, float* C, hipStream_t s);
+hipError_t launch_bwd_token(const moe_problem_t& p, const void* dout, const void* y,
+                            const int32_t* pos, const int32_t* topk_idx, const float* topk_w,
+                            const float* logits, const int32_t* counts, float g_aux, float g_z,
+                            void* dy, float* dl, hipStream_t s);
+hipError_t launch_bwd_dx(const moe_problem_t& p, const void* dxe, const int32_t* pos,
+                         const float* dl, const void* Wg, void* dx, hipStream_t s);
+hipError_t launch_bwd_colsum(const moe_problem_t& p, const void* rows, const int32_t* offsets,
+                             int N, float* out, hipStream_t s);
+int64_t bwd_gate_chunks(const moe_problem_t& p);
+hipError_t launch_bwd_gate(const moe_problem_t& p, const void* x, const float* dl, float* part,
+                           float* pb, float* dWg, float* dbg, hipStream_t s);
 // Expert choice on fp32 logits [T][E]: probs [T][E], sel [E][T/group][C],
 // rowof [T][E] (-1 where not taken) and offsets [E+1] (e * (T/group) * C).
 hipError_t launch_expert_choice(const moe_problem_t& p, int64_t group, int64_t C,

@@ -314,3 +314,57 @@ def test_ec_workspace_exact_size_and_null_event():
     assert ec_route(p, 64, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
     arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
     assert ec_forward(p, 64, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- training
+def fwd_train(p, ws_bytes=1 << 40, **kw):
+    a = dict(x=A, Wg=A, bg=None, W1=A, b1=None, W2=A, b2=None, out=A, losses=A, ws=A)
+    a.update(kw)
+    return moe.lib().moe_forward_train(ctypes.byref(p), a["x"], a["Wg"], a["bg"], a["W1"],
+                                       a["b1"], a["W2"], a["b2"], a["out"], a["losses"], a["ws"],
+                                       ws_bytes, None)
+
+
+def bwd(p, ws_bytes=1 << 40, g_aux=0.01, g_z=0.001, **kw):
+    a = dict(x=A, Wg=A, W1=A, W2=A, dout=A, dx=A, dWg=A, dbg=None, dW1=A, db1=None, dW2=A,
+             db2=None, ws=A)
+    a.update(kw)
+    return moe.lib().moe_backward(ctypes.byref(p), a["x"], a["Wg"], a["W1"], a["W2"], a["dout"],
+                                  g_aux, g_z, a["dx"], a["dWg"], a["dbg"], a["dW1"], a["db1"],
+                                  a["dW2"], a["db2"], a["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", BAD_PROBLEMS[:10] + [
+    (dict(dtype="f32"), moe.MOE_ERR_UNSUPPORTED),                 # bf16 only
+    (dict(T=2 ** 17, k=2, H=4096, F=4096), moe.MOE_ERR_UNSUPPORTED),  # 32-bit row ranges
+], ids=lambda v: str(v))
+def test_train_bad_problem_rejected(kw, status):
+    p = P(**kw)
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_train_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == status
+    assert fwd_train(p) == status
+    assert bwd(p) == status
+
+
+@pytest.mark.parametrize("arg", ["x", "Wg", "W1", "W2", "out", "losses", "ws"])
+def test_forward_train_null_required(arg):
+    assert fwd_train(P(), **{arg: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["x", "Wg", "W1", "W2", "dout", "dx", "dWg", "dW1", "dW2", "ws"])
+def test_backward_null_required(arg):
+    assert bwd(P(), **{arg: None}) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["x", "dout", "dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2"])
+def test_backward_misaligned(arg):
+    assert bwd(P(), **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_train_workspace_sizes_and_nan_weights():
+    p = P()
+    need = moe.moe_train_workspace_bytes(p)
+    assert need > moe.moe_workspace_bytes(p) and need % 256 == 0
+    assert fwd_train(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert bwd(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert bwd(p, g_aux=math.nan) == moe.MOE_ERR_INVALID_ARG
