@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step instead: moe_forward_train then moe_backward "
+                         "(aux and z loss weights 0.01 and 0.001), one JSON line")
     ap.add_argument("--no-abi-timing", action="store_true",
                     help="skip the per-call warm/cold timing that follows the timed steps "
                          "(thousands of extra launches; counter runs of the profiler omit it)")
@@ -281,6 +284,123 @@ def stage_timing(moe, torch, spec, prob, d, log_fn, min_iters=50, min_seconds=0.
     return res, A
 
 
+TRAIN_METRIC = "MoE layer training step (forward + backward) tokens/s on 1 MI355X"
+G_AUX, G_Z = 0.01, 0.001
+
+
+def train_bench(args, moe, torch, spec, inp, d, prob):
+    """A training step: moe_forward_train then moe_backward for a fixed seeded
+    upstream gradient; value = T / step time.  The roofline entry is the
+    backward's dominant GEMM launch against the bf16 MFMA peak, timed by the
+    library's own stage events."""
+    import numpy as np
+    import workloads as W
+    T, H, E, k, F = spec.T, spec.H, spec.E, spec.k, spec.F
+    cu = "cuda"
+    ws = torch.empty(moe.moe_train_workspace_bytes(prob), dtype=torch.uint8, device=cu)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=cu)
+    losses = torch.empty(2, dtype=torch.float32, device=cu)
+    dout = torch.from_numpy(W.synthetic_rows(spec, T, tid=98).view(np.int16)).to(cu).view(
+        torch.bfloat16)
+    f32 = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=cu)
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=cu)
+    dWg, dW1, dW2 = f32(H, E), f32(E, H, F), f32(E, F, H)
+    dbg = f32(E) if d["bg"] is not None else None
+    db1 = f32(E, F) if d["b1"] is not None else None
+    db2 = f32(E, H) if d["b2"] is not None else None
+    evs = [moe.StageEvents(moe.MOE_BACKWARD_EVENTS) for _ in range(args.steps)]
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def step(i=None):
+        if i is not None:
+            fev[i][0].record()
+        moe.moe_forward_train(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"],
+                              out, losses, ws)
+        if i is not None:
+            fev[i][1].record()
+        moe.moe_backward(prob, d["x"], d["Wg"], d["W1"], d["W2"], dout, G_AUX, G_Z, dx, dWg, dW1,
+                         dW2, ws, dbg=dbg, db1=db1, db2=db2,
+                         events=evs[i] if i is not None else None)
+
+    log(f"[bench] train warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} training steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
+    bst = np.array([e.stage_ms() for e in evs]).mean(axis=0)
+    sm = {n: float(v) for n, v in zip(moe.BACKWARD_STAGE_NAMES, bst)}
+    A = T * k                    # kept rows (the training workloads drop nothing)
+    gemm_flops = 2.0 * A * H * F
+    gemms = ("dgrad_da", "dgrad_dxe", "wgrad_w2", "wgrad_w1")
+    dom = max(gemms, key=lambda n: sm[n])
+    achieved = gemm_flops / (sm[dom] * 1e-3) / 1e12
+    bwd_ms = float(sum(bst))
+    res = {
+        "metric": TRAIN_METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded; random-init weights; seeded upstream gradient)",
+        "config": {"workload": spec.name, "T": T, "H": H, "E": E, "k": k, "F": F,
+                   "capacity_factor": spec.cf, "activation": spec.act,
+                   "g_aux": G_AUX, "g_z": G_Z},
+        "roofline": {"bound": "mfma", "kernel": f"bwd_{dom}", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "forward_train_ms": fwd_ms,
+        "backward_ms": bwd_ms,
+        "backward_stage_ms": sm,
+        "train_tflops": 6.0 * gemm_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
+        "backward_gemm_tflops": 4.0 * gemm_flops / (sum(sm[n] for n in gemms) * 1e-3) / 1e12,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle's backward on a bounded sample")
+        res["cpu_baseline"] = cpu_train_baseline(spec, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_train_baseline(spec, inp, target_s: float):
+    """The fp64 oracle's forward and backward (all gradients) on the first n
+    tokens taken as a problem of their own, n sized to about target_s, scaled
+    linearly to T (the work is per token)."""
+    import oracle as om
+    import workloads as W
+
+    def run(n):
+        sub = spec.replace(T=n)
+        si = dict(inp)
+        si["x"] = inp["x"][:n]
+        dout = W.synthetic_rows(sub, n, tid=98)
+        t1 = time.perf_counter()
+        om.backward(sub, si, dout, G_AUX, G_Z)
+        return time.perf_counter() - t1
+
+    threads = om.num_threads()
+    n0 = min(spec.T, 2 * threads)
+    t_probe = run(n0)
+    n = int(min(spec.T, max(n0, n0 * target_s / max(t_probe, 1e-6))))
+    t = run(n) if n > n0 else t_probe
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 C oracle backward (recomputing the forward), {threads} OpenMP "
+                       f"threads, on tokens 0..{n - 1} as a problem of their own ({t:.2f} s), "
+                       f"rate scaled linearly to {spec.T} tokens")}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -327,6 +447,9 @@ def main():
 
     d = {kk: dev(v) for kk, v in inp.items()}
     prob = moe.Problem.from_spec(spec)
+    if args.train:
+        train_bench(args, moe, torch, spec, inp, d, prob)
+        return
     g = spec.ec_group
     ws_bytes = moe.moe_ec_workspace_bytes(prob, g) if g else moe.moe_workspace_bytes(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

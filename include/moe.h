@@ -262,13 +262,31 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void
                                const void* b2, void* out, float* losses, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* Events recorded by moe_backward when `stage_events` is non-NULL, event i
+ * just before stage i starts, the last after the final stage. */
+enum {
+    MOE_BEV_TOKEN = 0,       /* dw, dy rows, the router's dl */
+    MOE_BEV_DGRAD_DA = 1,    /* da = (dy W2^T) * act'(a)   (one GEMM launch) */
+    MOE_BEV_DGRAD_DXE = 2,   /* da W1^T per kept row        (one GEMM launch) */
+    MOE_BEV_DX = 3,          /* dx = sum of kept rows + dl Wg^T */
+    MOE_BEV_GATHER = 4,      /* the kept rows of x */
+    MOE_BEV_WGRAD_W2 = 5,    /* dW2                          (one GEMM launch) */
+    MOE_BEV_WGRAD_W1 = 6,    /* dW1                          (one GEMM launch) */
+    MOE_BEV_BIAS = 7,        /* db1, db2 (empty when not asked for) */
+    MOE_BEV_GATE = 8,        /* dWg, dbg */
+    MOE_BEV_END = 9,
+    MOE_BACKWARD_EVENTS = 10
+};
+
 /* Gradients of L.  ws must hold the state of a moe_forward_train on the same
  * problem and inputs (nothing else may write it in between); biases are not
- * needed (the saved rows already include them). */
+ * needed (the saved rows already include them).  stage_events is NULL or an
+ * array of MOE_BACKWARD_EVENTS created events. */
 moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg, const void* W1,
                           const void* W2, const void* dout, float g_aux, float g_z, void* dx,
                           float* dWg, float* dbg, float* dW1, float* db1, float* dW2,
-                          float* db2, void* ws, size_t ws_bytes, hipStream_t stream);
+                          float* db2, void* ws, size_t ws_bytes, hipStream_t stream,
+                          hipEvent_t* stage_events);
 
 /* Static description of a status code (host). */
 const char* moe_status_string(moe_status_t s);

@@ -28,6 +28,9 @@ MOE_ROUTE_LOGITS_IN = 1
  MOE_EV_FFN_DOWN_FIXUP, MOE_EV_COMBINE, MOE_EV_END, MOE_FORWARD_EVENTS) = range(9)
 STAGE_NAMES = ("route", "permute", "ffn_up", "ffn_up_fixup", "ffn_down", "ffn_down_fixup",
                "combine")
+MOE_BACKWARD_EVENTS = 10
+BACKWARD_STAGE_NAMES = ("token", "dgrad_da", "dgrad_dxe", "dx", "gather", "wgrad_w2",
+                        "wgrad_w1", "bias", "gate")
 
 EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
@@ -104,7 +107,7 @@ def lib() -> ctypes.CDLL:
         L.moe_train_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_forward_train.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
         fl = ctypes.c_float
-        L.moe_backward.argtypes = [P] + [vp] * 5 + [fl, fl] + [vp] * 8 + [ctypes.c_size_t, vp]
+        L.moe_backward.argtypes = [P] + [vp] * 5 + [fl, fl] + [vp] * 8 + [ctypes.c_size_t, vp, vp]
         for f in ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
                   "moe_expert_ffn", "moe_combine", "moe_forward", "moe_ec_capacity",
                   "moe_ec_workspace_bytes", "moe_route_expert_choice",
@@ -255,11 +258,15 @@ def moe_forward_train(p: Problem, x, Wg, bg, W1, b1, W2, b2, out, losses, ws, st
 
 
 def moe_backward(p: Problem, x, Wg, W1, W2, dout, g_aux, g_z, dx, dWg, dW1, dW2, ws,
-                 dbg=None, db1=None, db2=None, stream=None) -> None:
+                 dbg=None, db1=None, db2=None, stream=None,
+                 events: Optional["StageEvents"] = None) -> None:
+    ev = events.array() if events is not None else None
     _check(lib().moe_backward(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(W1), _ptr(W2), _ptr(dout),
                               float(g_aux), float(g_z), _ptr(dx), _ptr(dWg), _ptr(dbg), _ptr(dW1),
                               _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(ws), _nbytes(ws),
-                              _stream(stream, dx)), "moe_backward")
+                              _stream(stream, dx),
+                              ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None),
+           "moe_backward")
 
 
 # ---------------------------------------------------------------- stage events
@@ -279,14 +286,16 @@ def _hiprt() -> ctypes.CDLL:
 
 
 class StageEvents:
-    """MOE_FORWARD_EVENTS HIP events for moe_forward(..., events=...): the
-    library records them on its stream around each stage, so stage times come
-    from the stream the kernels actually run on."""
+    """HIP events for moe_forward / moe_forward_expert_choice (n =
+    MOE_FORWARD_EVENTS, the default) or moe_backward (n = MOE_BACKWARD_EVENTS)
+    via events=...: the library records them on its stream around each stage,
+    so stage times come from the stream the kernels actually run on."""
 
-    def __init__(self):
+    def __init__(self, n: int = MOE_FORWARD_EVENTS):
         h = _hiprt()
-        self._ev = (ctypes.c_void_p * MOE_FORWARD_EVENTS)()
-        for i in range(MOE_FORWARD_EVENTS):
+        self.n = n
+        self._ev = (ctypes.c_void_p * n)()
+        for i in range(n):
             e = ctypes.c_void_p()
             if h.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -296,11 +305,11 @@ class StageEvents:
         return self._ev
 
     def stage_ms(self) -> Sequence[float]:
-        """Milliseconds of each stage of the last recorded forward (waits for it)."""
+        """Milliseconds of each stage of the last recorded call (waits for it)."""
         h = _hiprt()
-        h.hipEventSynchronize(self._ev[MOE_EV_END])
+        h.hipEventSynchronize(self._ev[self.n - 1])
         out = []
-        for i in range(MOE_FORWARD_EVENTS - 1):
+        for i in range(self.n - 1):
             ms = ctypes.c_float()
             if h.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -310,7 +319,7 @@ class StageEvents:
     def __del__(self):
         try:
             h = _hiprt()
-            for i in range(MOE_FORWARD_EVENTS):
+            for i in range(self.n):
                 if self._ev[i]:
                     h.hipEventDestroy(self._ev[i])
         except Exception:

@@ -132,12 +132,25 @@ __global__ __launch_bounds__(kBT) void bwd_dx(const u32x4_t* __restrict__ dxe,
                 acc[2 * q + 1] += bf16_hi(d[q]);
             }
         }
-        // gate term: the 8 hidden units h = 8 v .. 8 v + 7
+        // gate term: the 8 hidden units h = 8 v .. 8 v + 7, whose gate rows are
+        // 8 E contiguous elements of Wg: 16-byte loads when E % 8 == 0
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const uint16_t* wr = Wg + (8 * v + u) * E;
             float g = 0.f;
-            for (int e = 0; e < E; ++e) g = fmaf(s_dl[e], __uint_as_float((uint32_t)wr[e] << 16), g);
+            if ((E & 7) == 0) {
+                for (int e0 = 0; e0 < E; e0 += 8) {
+                    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wr + e0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        g = fmaf(s_dl[e0 + 2 * q], bf16_lo(wv[q]), g);
+                        g = fmaf(s_dl[e0 + 2 * q + 1], bf16_hi(wv[q]), g);
+                    }
+                }
+            } else {
+                for (int e = 0; e < E; ++e)
+                    g = fmaf(s_dl[e], __uint_as_float((uint32_t)wr[e] << 16), g);
+            }
             acc[u] += g;
         }
         u32x4_t o;
@@ -160,40 +173,64 @@ __global__ __launch_bounds__(256) void bwd_colsum(const uint16_t* __restrict__ r
     out[(int64_t)e * N + n] = acc;
 }
 
-// dWg partials: workgroup (column block of 256 hidden units, token chunk c,
-// expert block of kGateE): part[c][h][e] = sum over the chunk's tokens
-// (ascending) of x[t][h] dl[t][e]; the first column block also writes
-// pb[c][e] = sum of dl[t][e] over the chunk.
+// dWg partials: workgroup (block of 512 hidden units, token chunk c, expert
+// block of kGateE): part[c][h][e] = sum over the chunk's tokens (ascending) of
+// x[t][h] dl[t][e], two hidden units per thread; the x values of 8 tokens are
+// loaded before their products are added.  The first hidden-unit block also
+// writes pb[c][e] = sum of dl[t][e] over the chunk.
 constexpr int kGateE = 16;
+constexpr int kGateTok = 8;
 
 __global__ __launch_bounds__(256) void bwd_gate_partial(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ dl, int64_t T,
                                                         int H, int E, int64_t chunk,
                                                         float* __restrict__ part,
                                                         float* __restrict__ pb) {
-    const int h = blockIdx.x * 256 + threadIdx.x;
+    const int h = 2 * (blockIdx.x * 256 + threadIdx.x);     // H % 8 == 0: h + 1 < H with h
     const int c = blockIdx.y, e0 = blockIdx.z * kGateE;
     const int ne = min(kGateE, E - e0);
     const int64_t t0 = (int64_t)c * chunk, t1 = min(t0 + chunk, T);
-    float acc[kGateE];
+    float acc0[kGateE], acc1[kGateE];
 #pragma unroll
-    for (int j = 0; j < kGateE; ++j) acc[j] = 0.f;
+    for (int j = 0; j < kGateE; ++j) acc0[j] = acc1[j] = 0.f;
     if (h < H) {
-        for (int64_t t = t0; t < t1; ++t) {
-            const float xv = __uint_as_float((uint32_t)x[t * H + h] << 16);
+        for (int64_t tb = t0; tb < t1; tb += kGateTok) {
+            uint32_t xv[kGateTok];
 #pragma unroll
-            for (int j = 0; j < kGateE; ++j)
-                if (j < ne) acc[j] = fmaf(xv, dl[t * E + e0 + j], acc[j]);
+            for (int u = 0; u < kGateTok; ++u) {
+                const int64_t t = min(tb + u, t1 - 1);       // clamped, masked below
+                xv[u] = *reinterpret_cast<const uint32_t*>(x + t * H + h);
+            }
+#pragma unroll
+            for (int u = 0; u < kGateTok; ++u) {
+                if (tb + u >= t1) break;
+                const float* d = dl + (tb + u) * E + e0;
+                const float x0 = bf16_lo(xv[u]), x1 = bf16_hi(xv[u]);
+#pragma unroll
+                for (int j = 0; j < kGateE; ++j) {
+                    if (j < ne) {
+                        acc0[j] = fmaf(x0, d[j], acc0[j]);
+                        acc1[j] = fmaf(x1, d[j], acc1[j]);
+                    }
+                }
+            }
         }
         float* o = part + ((int64_t)c * H + h) * E + e0;
 #pragma unroll
         for (int j = 0; j < kGateE; ++j)
-            if (j < ne) o[j] = acc[j];
+            if (j < ne) {
+                o[j] = acc0[j];
+                o[E + j] = acc1[j];
+            }
     }
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)ne) {
-        float b = 0.f;
-        for (int64_t t = t0; t < t1; ++t) b += dl[t * E + e0 + threadIdx.x];
-        pb[(int64_t)c * E + e0 + threadIdx.x] = b;
+    if (blockIdx.x == 0) {                                // uniform over the workgroup
+        __shared__ float red[256 / 64];
+        for (int j = 0; j < ne; ++j) {
+            float b = 0.f;
+            for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) b += dl[t * E + e0 + j];
+            b = block_sum(b, red);
+            if (threadIdx.x == 0) pb[(int64_t)c * E + e0 + j] = b;
+        }
     }
 }
 
@@ -251,7 +288,7 @@ hipError_t launch_bwd_gate(const moe_problem_t& p, const void* x, const float* d
                            float* pb, float* dWg, float* dbg, hipStream_t s) {
     const int64_t nchunk = bwd_gate_chunks(p);
     const int64_t chunk = (p.T + nchunk - 1) / nchunk;
-    const dim3 g1((unsigned)((p.H + 255) / 256), (unsigned)nchunk,
+    const dim3 g1((unsigned)((p.H + 511) / 512), (unsigned)nchunk,
                   (unsigned)((p.E + kGateE - 1) / kGateE));
     bwd_gate_partial<<<g1, dim3(256), 0, s>>>(static_cast<const uint16_t*>(x), dl, p.T, p.H, p.E,
                                                chunk, part, pb);

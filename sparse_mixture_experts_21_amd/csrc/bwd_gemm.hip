@@ -191,7 +191,13 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
 // Workgroup p: row tile p / Nt (over the experts' kept rows, 256 rows each,
 // never straddling experts) x column tile p % Nt.  EPI_DA: multiply by
 // act'(pre[r][n]); EPI_PLAIN: store as is.  Output bf16 [rows][N].
+// The epilogue works on the tile in LDS ([m][n] bf16, 528-byte pitch, as the
+// forward's): with EPI_DA the pre-activation tile is first loaded there by
+// whole rows, each lane replaces its 4 x 4 x 16 values by the products, and the
+// tile is written out by whole rows.
 enum { kEpiPlain = 0, kEpiDa = 1 };
+constexpr int kOutPitch = kT * 2 + 16;
+constexpr int kDgradLds = kLds > kT * kOutPitch ? kLds : kT * kOutPitch;
 
 template <int EPI, int ACT>
 __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                                                  const uint16_t* __restrict__ Bw,
                                                  const uint16_t* __restrict__ pre,
                                                  uint16_t* __restrict__ C, int K, int N, int Nt) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    __shared__ __attribute__((aligned(1024))) char lds[kDgradLds];
     const int p = blockIdx.x;
     const int mt = p / Nt, nt = p % Nt;
     int e, m0, row_begin, n_rows;
@@ -221,24 +227,34 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
     zero(acc);
     bwd_mainloop<kRow, kRow>(a, b, (K + kBK - 1) / kBK, lds, acc);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     const int l32 = lane & 31, half = lane >> 5;
+    const int chunks = min(kT, N - n0) / 8;             // 16-byte chunks per row (N % 8 == 0)
+    const int64_t base = (int64_t)(row_begin + m0) * N + n0;
+    lds_barrier();
+    if constexpr (EPI == kEpiDa) {
+        for (int idx = tid; idx < kT * (kT / 8); idx += 256) {
+            const int r = idx / (kT / 8), c = idx % (kT / 8);
+            if (r < rows && c < chunks)
+                *reinterpret_cast<u32x4_t*>(lds + r * kOutPitch + c * 16) =
+                    *reinterpret_cast<const u32x4_t*>(pre + base + (int64_t)r * N + c * 8);
+        }
+        lds_barrier();
+    }
 #pragma unroll
     for (int j = 0; j < kF; ++j) {
         const int m = 128 * wm + 32 * j + l32;
-        if (m >= rows) continue;
-        const int64_t row = (int64_t)(row_begin + m0 + m) * N;
 #pragma unroll
         for (int i = 0; i < kF; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + 128 * wn + 32 * i + 8 * g + 4 * half;
-                if (n >= N) continue;                       // N % 8 == 0: all 4 columns valid
+                const int nl = 128 * wn + 32 * i + 8 * g + 4 * half;
+                char* slot = lds + m * kOutPitch + nl * 2;
                 float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                               acc[i][j][4 * g + 3]};
                 if constexpr (EPI == kEpiDa) {
-                    const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(pre + row + n);
+                    const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(slot);
                     v[0] *= activate_grad<ACT>(bf16_lo(pa[0]));
                     v[1] *= activate_grad<ACT>(bf16_hi(pa[0]));
                     v[2] *= activate_grad<ACT>(bf16_lo(pa[1]));
@@ -247,8 +263,15 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                 u32x2_t o;
                 o[0] = pack_bf16x2(v[0], v[1]);
                 o[1] = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<u32x2_t*>(C + row + n) = o;
+                *reinterpret_cast<u32x2_t*>(slot) = o;
             }
+    }
+    lds_barrier();
+    for (int idx = tid; idx < kT * (kT / 8); idx += 256) {
+        const int r = idx / (kT / 8), c = idx % (kT / 8);
+        if (r < rows && c < chunks)
+            *reinterpret_cast<u32x4_t*>(C + base + (int64_t)r * N + c * 8) =
+                *reinterpret_cast<const u32x4_t*>(lds + r * kOutPitch + c * 16);
     }
 }
 

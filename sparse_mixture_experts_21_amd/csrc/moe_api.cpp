@@ -501,11 +501,16 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void
 moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg, const void* W1,
                           const void* W2, const void* dout, float g_aux, float g_z, void* dx,
                           float* dWg, float* dbg, float* dW1, float* db1, float* dW2, float* db2,
-                          void* ws, size_t ws_bytes, hipStream_t stream) {
+                          void* ws, size_t ws_bytes, hipStream_t stream,
+                          hipEvent_t* stage_events) {
     moe_status_t st = check_train(p);
     if (st != MOE_OK) return st;
     if (!x || !Wg || !W1 || !W2 || !dout || !dx || !dWg || !dW1 || !dW2 || !ws)
         return MOE_ERR_INVALID_ARG;
+    if (stage_events) {
+        for (int i = 0; i < MOE_BACKWARD_EVENTS; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    }
     if (std::isnan(g_aux) || std::isnan(g_z)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W2) || !aligned16(dout) ||
         !aligned16(dx) || !aligned16(dWg) || !opt_ok(dbg) || !aligned16(dW1) || !opt_ok(db1) ||
@@ -528,21 +533,34 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg,
     void* xp = w + X.xp;
     const int H = p->H, F = p->F;
 
+    auto ev = [&](int i) -> hipError_t {
+        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+    };
     // dw, dy rows and the router's dl; then the two data-gradient GEMMs and dx
-    hipError_t e = launch_bwd_token(*p, dout, w + L.y, ps, idx, tw, lg, cnt, g_aux, g_z, dy, dl,
-                                    stream);
+    hipError_t e = ev(MOE_BEV_TOKEN);
+    if (e == hipSuccess)
+        e = launch_bwd_token(*p, dout, w + L.y, ps, idx, tw, lg, cnt, g_aux, g_z, dy, dl, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_DGRAD_DA);
     if (e == hipSuccess) e = launch_bwd_dgrad(*p, true, dy, off, W2, w + X.a, da, H, F, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_DGRAD_DXE);
     if (e == hipSuccess) e = launch_bwd_dgrad(*p, false, da, off, W1, nullptr, dxe, F, H, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_DX);
     if (e == hipSuccess) e = launch_bwd_dx(*p, dxe, ps, dl, Wg, dx, stream);
     // weight gradients
+    if (e == hipSuccess) e = ev(MOE_BEV_GATHER);
     if (e == hipSuccess) e = launch_gather(*p, x, ps, xp, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_WGRAD_W2);
     if (e == hipSuccess) e = launch_bwd_wgrad(*p, w + L.h, dy, off, F, H, dW2, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_WGRAD_W1);
     if (e == hipSuccess) e = launch_bwd_wgrad(*p, xp, da, off, H, F, dW1, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_BIAS);
     if (e == hipSuccess && db2) e = launch_bwd_colsum(*p, dy, off, H, db2, stream);
     if (e == hipSuccess && db1) e = launch_bwd_colsum(*p, da, off, F, db1, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_GATE);
     if (e == hipSuccess)
         e = launch_bwd_gate(*p, x, dl, reinterpret_cast<float*>(w + X.gpart),
                             reinterpret_cast<float*>(w + X.gpb), dWg, dbg, stream);
+    if (e == hipSuccess) e = ev(MOE_BEV_END);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -331,7 +331,7 @@ def bwd(p, ws_bytes=1 << 40, g_aux=0.01, g_z=0.001, **kw):
     a.update(kw)
     return moe.lib().moe_backward(ctypes.byref(p), a["x"], a["Wg"], a["W1"], a["W2"], a["dout"],
                                   g_aux, g_z, a["dx"], a["dWg"], a["dbg"], a["dW1"], a["db1"],
-                                  a["dW2"], a["db2"], a["ws"], ws_bytes, None)
+                                  a["dW2"], a["db2"], a["ws"], ws_bytes, None, a.get("ev"))
 
 
 @pytest.mark.parametrize("kw,status", BAD_PROBLEMS[:10] + [
@@ -368,3 +368,5 @@ def test_train_workspace_sizes_and_nan_weights():
     assert fwd_train(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert bwd(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert bwd(p, g_aux=math.nan) == moe.MOE_ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * moe.MOE_BACKWARD_EVENTS)()
+    assert bwd(p, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
