@@ -19,8 +19,9 @@
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, issued as
 // D[n][m] = W^T[n][k] . X^T[k][m] so each lane of the epilogue owns 4
 // consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
-// buffer_load ... lds (no VGPR staging) through 4 LDS stages of a 32-deep
-// k-tile, issued 3 k-tiles ahead of the MFMAs.  The weights stay in their
+// buffer_load ... lds (no VGPR staging) through a ring of LDS stages (2 of
+// 64-deep k-tiles for 256-row tiles, 4 of 32-deep ones for the narrower
+// layouts), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
 // natural [k][n] layout in LDS and are turned into K-contiguous MFMA
 // fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
 // fragment reads for the next k-substep are interleaved with the MFMAs of
@@ -38,16 +39,14 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- bf16 MFMA
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
-#endif
-#ifndef MOE_GEMM_NS
-#define MOE_GEMM_NS 4
-#endif
+// k-tile depth and LDS stages: the 256-row layout takes 64-deep k-tiles in 2
+// stages (one barrier per 64 k, 128 KB of LDS); the narrower layouts, which
+// stream weights, keep 32-deep k-tiles in 4 stages (prefetch 3 k-tiles ahead).
 template <int BM>
 struct Cfg {
-    static constexpr int BN = 256, BK = MOE_GEMM_BK;  // k-tile depth
-    static constexpr int NS = MOE_GEMM_NS;            // LDS stages
+    static constexpr int BN = 256;
+    static constexpr int BK = BM == 256 ? 64 : 32;    // k-tile depth
+    static constexpr int NS = BM == 256 ? 2 : 4;      // LDS stages
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
@@ -506,13 +505,15 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
 
 // One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
 template <int TB, int ACT, bool NTW, bool SAVE>
-__device__ __forceinline__ void whole_tile(const TileRef& tr, int nk, char* lds,
+__device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
                                            const uint16_t* __restrict__ X, uint32_t x_bytes,
                                            const int32_t* __restrict__ rowmap,
                                            const uint16_t* __restrict__ W,
                                            const uint16_t* __restrict__ bias,
                                            uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
                                            int K, int N) {
+    // k-tiles of this layout's own depth (the layouts differ in k-tile depth)
+    const int nk = (K + Cfg<TB>::BK - 1) / Cfg<TB>::BK;
     f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
     zero_acc<TB>(acc);
     gemm_mainloop<TB, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
@@ -532,6 +533,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
     int K, int N, int Nt, int SBN, int ncu, float* __restrict__ part) {
     using G = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
+    static_assert(BM < 128 || Cfg<64>::LDS_BYTES <= G::LDS_BYTES, "64-row layout fits");
+    static_assert(BM < 256 || Cfg<128>::LDS_BYTES <= G::LDS_BYTES, "128-row layout fits");
     // With at most 128 rows per tile (few rows per expert) an expert's weights
     // are read about once, so they stream past the last-level cache instead of
     // evicting (and writing back) other kernels' lines; the 256-row layout
@@ -558,19 +561,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         const int rows = tr.n_rows - tr.m0;
         if constexpr (BM >= 128) {
             if (rows <= 64) {
-                whole_tile<64, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                whole_tile<64, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
                                                   N);
                 return;
             }
         }
         if constexpr (BM >= 256) {
             if (rows <= 128) {
-                whole_tile<128, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                whole_tile<128, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
                                                    N);
                 return;
             }
         }
-        whole_tile<BM, ACT, kNtW, SAVE>(tr, nk, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
+        whole_tile<BM, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
         return;
     }
     f32x16_t acc[G::FN][G::FM];
