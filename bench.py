@@ -65,7 +65,7 @@ def log(*a):
 
 
 # the sources that define the expert GEMM kernels the traffic counters describe
-GEMM_SOURCES = ("expert_gemm.hip", "lds_dma.h", "moe_internal.h")
+GEMM_SOURCES = ("expert_gemm.hip", "gemm_common.h", "lds_dma.h", "moe_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -131,8 +131,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int =
     for k in sorted(fetch):
         if "ffn_gemm_bf16" not in k:
             continue
-        # template arguments <BM, activation>: activation 0 is the second GEMM
-        name = "ffn_gemm_bf16_down" if k.split(">")[0].endswith(" 0") else "ffn_gemm_bf16_up"
+        # template arguments <BM, activation, save>: activation 0 is the second GEMM
+        targs = [a.strip() for a in k.split("<", 1)[1].split(">")[0].split(",")]
+        name = "ffn_gemm_bf16_down" if targs[1] == "0" else "ffn_gemm_bf16_up"
         hbm = (fetch[k] / f_fetch + write.get(k, 0.0) / f_write) * 1024.0
         out["kernels"][name] = {"symbol": k, "fetch_kib": fetch[k], "write_kib": write.get(k),
                                 "hbm_bytes": hbm}
