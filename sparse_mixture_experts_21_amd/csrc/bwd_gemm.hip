@@ -10,7 +10,7 @@
 //
 // The tile machinery is the forward's: 256 x 256 output tiles, 4 waves of
 // 128 x 128 on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, operands moved
-// HBM -> LDS by buffer_load ... lds through 4 stages of a 32-deep k-tile.  An
+// HBM -> LDS by buffer_load ... lds through 2 stages of a 64-deep k-tile.  An
 // operand is either K-contiguous ("row" layout: LDS [idx][k], 64-byte rows,
 // plain 16-byte fragment reads) or row-major over k ("k-major": LDS [k][idx],
 // 512-byte rows, ds_read_b64_tr_b16 transposed fragment reads).  dgrad uses
@@ -26,13 +26,19 @@ namespace moe {
 namespace {
 
 constexpr int kT = 256;                 // tile edge (both output dimensions)
-constexpr int kBK = 32;                 // k-tile depth
-constexpr int kNS = 4;                  // LDS stages
-constexpr int kOpBytes = kT * kBK * 2;  // one operand tile per stage: 16 KB
+#ifndef MOE_BWD_BK
+#define MOE_BWD_BK 64
+#endif
+constexpr int kBK = MOE_BWD_BK;         // k-tile depth
+constexpr int kNS = kBK == 64 ? 2 : 4;  // LDS stages (128 KB either way)
+constexpr int kOpBytes = kT * kBK * 2;  // one operand tile per stage
 constexpr int kStage = 2 * kOpBytes;
-constexpr int kLds = kNS * kStage;      // 128 KB
+constexpr int kLds = kNS * kStage;
 constexpr int kF = 4;                   // 32 x 32 MFMA tiles per wave and dimension
 constexpr int kDmaPerOp = kOpBytes / 4096;   // 1 KB DMA blocks per wave per operand
+// row layout: 16-byte chunks per row, rows per 1 KB block, swizzle shift
+constexpr int kCpr = kBK / 8, kRpb = 64 / kCpr, kRsh = kCpr == 4 ? 2 : 1;
+static_assert(kBK == 32 || kBK == 64, "k-tile depth");
 
 enum Layout { kRow = 0, kKmaj = 1 };
 
@@ -58,9 +64,10 @@ __device__ __forceinline__ uint32_t dma_src(const Operand& o, int q, int t) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int blk = 4 * q + wave;                       // 1 KB block of the stage tile
     if constexpr (L == kRow) {
-        // 16 rows of 64 bytes per block; chunk c of row idx stored at c ^ ((idx >> 2) & 3)
-        const int idx = 16 * blk + (lane >> 2);
-        const int c = (lane & 3) ^ ((idx >> 2) & 3);
+        // kRpb rows of 2 kBK bytes per block; chunk c of row idx stored at
+        // c ^ ((idx >> kRsh) % kCpr)
+        const int idx = kRpb * blk + lane / kCpr;
+        const int c = (lane % kCpr) ^ ((idx >> kRsh) % kCpr);
         const int k = t * kBK + 8 * c;
         if (idx >= o.n_idx || k >= o.n_k) return kOob;
         return (uint32_t)idx * o.ld + (uint32_t)k * 2u;
@@ -82,7 +89,7 @@ __device__ __forceinline__ uint32_t frag_addr(int w0, int f, int kk) {
     const int lane = threadIdx.x & 63;
     if constexpr (L == kRow) {
         const int idx = w0 + 32 * f + (lane & 31);
-        const int pc = (2 * kk + (lane >> 5)) ^ ((idx >> 2) & 3);
+        const int pc = (2 * kk + (lane >> 5)) ^ ((idx >> kRsh) % kCpr);
         return (uint32_t)(idx * kBK * 2 + pc * 16);
     } else {
         const int grp = lane >> 4, s16 = lane & 15;
@@ -108,7 +115,12 @@ __device__ __forceinline__ bf16x8_t read_frag(uint32_t a) {
 
 // acc[i][j] += A-side fragments i (wave column half) x B-side fragments j
 // (wave row half) over nk k-tiles.  A: first MFMA operand (output columns),
-// B: second (output rows).
+// B: second (output rows).  The schedule is the forward GEMM's: DMA runs
+// kNS - 1 k-tiles ahead, a k-tile's DMAs are spread one at a time between
+// MFMA groups over two substeps (H1 after the barrier that frees their stage,
+// H2 in the next substep), and the fragments of the next substep are read
+// between the current substep's MFMAs (scheduling groups), with one barrier
+// per k-tile.
 template <int LA, int LB>
 __device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B, int nk,
                                              char* lds, f32x16_t (&acc)[kF][kF]) {
@@ -118,38 +130,44 @@ __device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B,
     constexpr int NDMA = 2 * kDmaPerOp;
     auto issue_one = [&](int t, int q) {
         const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
-        const int wave_ = threadIdx.x >> 6;
         if (q < kDmaPerOp) {
-            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave_) * 1024));
+            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024));
             dma16(A.rsrc, dma_src<LA>(A, q, t), l);
         } else {
             const int qb = q - kDmaPerOp;
             const uint32_t l = __builtin_amdgcn_readfirstlane(
-                st + (uint32_t)(kOpBytes + (4 * qb + wave_) * 1024));
+                st + (uint32_t)(kOpBytes + (4 * qb + wave) * 1024));
             dma16(B.rsrc, dma_src<LB>(B, qb, t), l);
         }
     };
     bf16x8_t fa[2][kF], fb[2][kF];
-    auto read_frags = [&](int t, int kk, int buf) {
+    // fragment f (f < kF: A side, else B side) of substep kk of k-tile t
+    auto read_one = [&](int t, int kk, int buf, int f) {
         const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
-#pragma unroll
-        for (int f = 0; f < kF; ++f) fa[buf][f] = read_frag<LA>(st + frag_addr<LA>(128 * wn, f, kk));
-#pragma unroll
-        for (int f = 0; f < kF; ++f)
-            fb[buf][f] = read_frag<LB>(st + kOpBytes + frag_addr<LB>(128 * wm, f, kk));
+        if (f < kF) fa[buf][f] = read_frag<LA>(st + frag_addr<LA>(128 * wn, f, kk));
+        else fb[buf][f - kF] = read_frag<LB>(st + kOpBytes + frag_addr<LB>(128 * wm, f - kF, kk));
     };
-    auto mfma = [&](int buf) {
+    // fragments in the order the MFMAs consume them: A0, B0..B3, A1..A3
+    auto frag_id = [](int o) { return o == 0 ? 0 : (o <= kF ? kF + o - 1 : o - kF); };
+    auto read_all = [&](int t, int kk, int buf) {
 #pragma unroll
-        for (int i = 0; i < kF; ++i)
-#pragma unroll
-            for (int j = 0; j < kF; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
-                                                                    acc[i][j], 0, 0, 0);
+        for (int o = 0; o < 2 * kF; ++o) read_one(t, kk, buf, frag_id(o));
     };
-
-    // DMA runs NS-1 k-tiles ahead: half of a k-tile's DMAs are issued after the
-    // barrier that frees their stage, the other half during the next substep.
-    constexpr int H1 = NDMA / 2, H2 = NDMA - H1;
+    auto mfma_range = [&](int buf, int lo, int hi) {
+#pragma unroll
+        for (int x = 0; x < kF * kF; ++x) {
+            if (x < lo || x >= hi) continue;
+            const int i = x / kF, j = x % kF;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
+                                                                acc[i][j], 0, 0, 0);
+        }
+    };
+    constexpr int NMF = kF * kF;
+    constexpr int NRD = (LA == kKmaj ? 2 : 1) * kF + (LB == kKmaj ? 2 : 1) * kF;
+    constexpr int NF = 2 * kF;
+    constexpr int H1 = (NDMA + 1) / 2, H2 = NDMA - H1;
+    constexpr int NSUB = kBK / 16;
+    constexpr int RG2 = H2 > 1 ? H2 / 2 : 1, RG1 = H1 > 1 ? H1 / 2 : 1;
 #pragma unroll
     for (int t = 0; t + 1 < kNS; ++t)
 #pragma unroll
@@ -158,22 +176,61 @@ __device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B,
     for (int q = 0; q < H1; ++q) issue_one(kNS - 1, q);
     wait_vmcnt<(kNS - 2) * NDMA + H1>();
     lds_barrier();
-    read_frags(0, 0, 0);
+    read_all(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-        // substep 0 MFMAs, substep 1 fragments, the rest of k-tile kt+NS-1's DMAs
+        // substep 0: MFMAs || fragments of substep 1 || the rest of k-tile kt+NS-1's DMAs
 #pragma unroll
-        for (int q = 0; q < H2; ++q) issue_one(kt + kNS - 1, H1 + q);
-        read_frags(kt, 1, 1);
-        mfma(0);
+        for (int g = 0; g < H2; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(kt + kNS - 1, H1 + g);
+            mfma_range(0, g * NMF / H2, (g + 1) * NMF / H2);
+            if (g < RG2) {
+#pragma unroll
+                for (int o = g * NF / RG2; o < (g + 1) * NF / RG2; ++o)
+                    read_one(kt, 1, 1, frag_id(o));
+            }
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
+        // substeps 1..NSUB-2
+#pragma unroll
+        for (int sub = 1; sub + 1 < NSUB; ++sub) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_all(kt, sub + 1, (sub + 1) & 1);
+            mfma_range(sub & 1, 0, NMF);
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // k-tile kt+1 has landed for every wave; stage kt % NS is free again
         wait_vmcnt<(kNS - 2) * NDMA>();
         wait_lgkm0();
         lds_barrier();
+        // last substep: MFMAs || first fragments of k-tile kt+1 || DMAs of k-tile kt+NS
 #pragma unroll
-        for (int q = 0; q < H1; ++q) issue_one(kt + kNS, q);
-        read_frags(kt + 1, 0, 0);
-        mfma(1);
+        for (int g = 0; g < H1; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(kt + kNS, g);
+            mfma_range((NSUB - 1) & 1, g * NMF / H1, (g + 1) * NMF / H1);
+            if (g < RG1) {
+#pragma unroll
+                for (int o = g * NF / RG1; o < (g + 1) * NF / RG1; ++o)
+                    read_one(kt + 1, 0, 0, frag_id(o));
+            }
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
     wait_lgkm0();
 }
@@ -204,10 +261,15 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                                                  const int32_t* __restrict__ offsets, int E,
                                                  const uint16_t* __restrict__ Bw,
                                                  const uint16_t* __restrict__ pre,
-                                                 uint16_t* __restrict__ C, int K, int N, int Nt) {
+                                                 uint16_t* __restrict__ C, int K, int N, int Nt,
+                                                 int SBN) {
     __shared__ __attribute__((aligned(1024))) char lds[kDgradLds];
     const int p = blockIdx.x;
-    const int mt = p / Nt, nt = p % Nt;
+    // the forward GEMM's XCD-aware order over the real tiles
+    const int real_mt = __builtin_amdgcn_readfirstlane(real_row_tiles<kT>(offsets, E));
+    if (p >= real_mt * Nt) return;
+    int mt, nt;
+    dense_coords(p, real_mt, Nt, SBN, mt, nt);
     int e, m0, row_begin, n_rows;
     if (!find_tile<kT>(offsets, E, mt, e, m0, row_begin, n_rows)) return;
     const int n0 = nt * kT;
@@ -282,11 +344,15 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
 __global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
                                                  const uint16_t* __restrict__ Q,
                                                  const int32_t* __restrict__ offsets, int I,
-                                                 int J, int It, int Jt, float* __restrict__ C) {
+                                                 int J, int It, int Jt, int E, int SBN,
+                                                 float* __restrict__ C) {
     __shared__ __attribute__((aligned(1024))) char lds[kLds];
-    const int p = blockIdx.x;
-    const int e = p / (It * Jt), ij = p % (It * Jt);
-    const int i0 = (ij / Jt) * kT, j0 = (ij % Jt) * kT;
+    // tile rows are (expert, i) pairs, expert-major; the forward GEMM's
+    // XCD-aware order over them and the j tiles
+    int mt, nt;
+    dense_coords(blockIdx.x, E * It, Jt, SBN, mt, nt);
+    const int e = mt / It;
+    const int i0 = (mt % It) * kT, j0 = nt * kT;
     const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
     const int nr = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - r0;
     Operand a, b;
@@ -333,25 +399,31 @@ hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, cons
     const int64_t rows = p.T * p.k;
     const int Mt = (int)((rows + kT - 1) / kT + p.E);          // row tiles, worst case
     const int Nt = (N + kT - 1) / kT;
+    const int SBN = (Nt % 16 == 0) ? 16 : (Nt % 8 == 0) ? 8 : 4;
     const dim3 grid((unsigned)((int64_t)Mt * Nt)), block(256);
     auto* x = static_cast<const uint16_t*>(X);
     auto* b = static_cast<const uint16_t*>(Bw);
     auto* pr = static_cast<const uint16_t*>(pre);
     auto* c = static_cast<uint16_t*>(C);
     if (!da)
-        bwd_dgrad<kEpiPlain, kActNone><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+        bwd_dgrad<kEpiPlain, kActNone><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
+                                                                  SBN);
     else if (p.activation == MOE_ACT_SILU)
-        bwd_dgrad<kEpiDa, kActSilu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+        bwd_dgrad<kEpiDa, kActSilu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
+                                                                  SBN);
     else
-        bwd_dgrad<kEpiDa, kActGelu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt);
+        bwd_dgrad<kEpiDa, kActGelu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
+                                                                  SBN);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_wgrad(const moe_problem_t& p, const void* P, const void* Q,
                             const int32_t* offsets, int I, int J, float* C, hipStream_t s) {
     const int It = (I + kT - 1) / kT, Jt = (J + kT - 1) / kT;
+    const int SBN = (Jt % 16 == 0) ? 16 : (Jt % 8 == 0) ? 8 : 4;
     bwd_wgrad<<<dim3((unsigned)(p.E * It * Jt)), dim3(256), 0, s>>>(
-        static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(Q), offsets, I, J, It, Jt, C);
+        static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(Q), offsets, I, J, It, Jt,
+        p.E, SBN, C);
     return hipGetLastError();
 }
 

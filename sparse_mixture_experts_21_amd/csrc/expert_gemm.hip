@@ -72,49 +72,6 @@ typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
-// Tile order.  Real tiles get the dense positions 0 .. R-1 (R = real row tiles
-// x Nt; the real row-tile count is computed on the device from `offsets`).
-// Full super-block rows come first: super-blocks of 256 tiles (SBM = 256/SBN
-// row tiles x SBN column tiles, one tile per CU), walked row-major.  The
-// hardware deals workgroups to the 8 XCDs round-robin, so position p runs on
-// XCD p % 8; in each super-block every XCD gets an 8 x 4 sub-block (rotating
-// with the super-block index), so the ~32 tiles resident on one XCD share
-// their row and weight slabs in its L2, and slabs another XCD already pulled
-// come from the memory-side cache.  The remaining (< SBM) row tiles follow,
-// XCD x taking the column tiles nt = x (mod 8) when Nt % 8 == 0.
-__device__ __forceinline__ void dense_coords(int p, int real_mt, int Nt, int SBN, int& mt,
-                                             int& nt) {
-    const int SBM = 256 / SBN;
-    if (Nt % SBN != 0) {                                  // no super-blocks (narrow N)
-        mt = p / Nt;
-        nt = p % Nt;
-        return;
-    }
-    const int F = real_mt / SBM;                          // full super-block rows
-    const int nfull = F * SBM * Nt;
-    if (p < nfull) {
-        const int sb = p >> 8, q = p & 255;
-        const int x = q & 7, j = q >> 3;                  // XCD, slot on the XCD
-        const int nsbn = Nt / SBN;
-        const int sbm = sb / nsbn, sbn = sb % nsbn;
-        // XCD x takes sub-block (x + sb) % 8
-        const int s8 = (x + sb) & 7;
-        const int xm = s8 % (SBM / 8), xn = s8 / (SBM / 8);
-        mt = sbm * SBM + xm * 8 + (j & 7);
-        nt = sbn * SBN + xn * 4 + (j >> 3);
-        return;
-    }
-    const int q = p - nfull, rem = real_mt - F * SBM;
-    if (Nt % 8 == 0) {
-        const int x = q & 7, j = q >> 3;
-        nt = 8 * (j / rem) + x;
-        mt = F * SBM + j % rem;
-    } else {
-        mt = F * SBM + q / Nt;
-        nt = q % Nt;
-    }
-}
-
 // The last (R mod ncu) tiles would leave most CUs idle in a final, ragged
 // round.  When they are at most half a round, each of them is cut along K into
 // S = ncu / tail slices (at most kMaxUnits slices in all, each at least NS
