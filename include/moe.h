@@ -256,7 +256,9 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, co
 moe_status_t moe_train_workspace_bytes(const moe_problem_t* p, size_t* bytes /* host */);
 
 /* moe_forward (out, losses) that keeps in ws what moe_backward needs: the fp32
- * logits, routing, dispatch, the pre-activation rows a and the h and y rows. */
+ * logits, routing, dispatch, the h and y rows, and act'(a), the activation's
+ * derivative at the first Linear's pre-activation a (fp32, with bias),
+ * evaluated with act(a) and stored as bf16 rows. */
 moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void* Wg,
                                const void* bg, const void* W1, const void* b1, const void* W2,
                                const void* b2, void* out, float* losses, void* ws,
@@ -266,7 +268,7 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void
  * just before stage i starts, the last after the final stage. */
 enum {
     MOE_BEV_TOKEN = 0,       /* dw, dy rows, the router's dl */
-    MOE_BEV_DGRAD_DA = 1,    /* da = (dy W2^T) * act'(a)   (one GEMM launch) */
+    MOE_BEV_DGRAD_DA = 1,    /* da = (dy W2^T) * act'(a), act'(a) saved  (one GEMM launch) */
     MOE_BEV_DGRAD_DXE = 2,   /* da W1^T per kept row        (one GEMM launch) */
     MOE_BEV_DX = 3,          /* dx = sum of kept rows + dl Wg^T */
     MOE_BEV_GATHER = 4,      /* the kept rows of x */

@@ -3,7 +3,8 @@
 // rows r of expert e (offsets[e] <= r < offsets[e+1]):
 //
 //   dgrad   C[r][n] = sum_k X[r][k] B[e][n][k]      both operands K-contiguous
-//           (da = (dy . W2[e]^T) * act'(a):  X = dy, B = W2[e] = [F][H], K = H;
+//           (da = (dy . W2[e]^T) * act'(a), act'(a) saved by the forward:
+//                                            X = dy, B = W2[e] = [F][H], K = H;
 //            dxe = da . W1[e]^T:            X = da, B = W1[e] = [H][F], K = F)
 //   wgrad   C[e][i][j] = sum_r P[r][i] Q[r][j]       both operands row-major over r
 //           (dW2[e] = h^T dy:  P = h, Q = dy;  dW1[e] = xp^T da:  P = xp, Q = da)
@@ -245,22 +246,23 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
 }
 
 // ---------------------------------------------------------------- dgrad
-// Workgroup p: row tile p / Nt (over the experts' kept rows, 256 rows each,
-// never straddling experts) x column tile p % Nt.  EPI_DA: multiply by
-// act'(pre[r][n]); EPI_PLAIN: store as is.  Output bf16 [rows][N].
+// Workgroup p: a row tile (over the experts' kept rows, 256 rows each, never
+// straddling experts) x a column tile, in the forward GEMM's tile order.
+// EPI_DA: multiply by gp[r][n] = act'(a[r][n]), saved by the training
+// forward's first GEMM; EPI_PLAIN: store as is.  Output bf16 [rows][N].
 // The epilogue works on the tile in LDS ([m][n] bf16, 528-byte pitch, as the
-// forward's): with EPI_DA the pre-activation tile is first loaded there by
-// whole rows, each lane replaces its 4 x 4 x 16 values by the products, and the
-// tile is written out by whole rows.
+// forward's): with EPI_DA the act' tile is first loaded there by whole rows,
+// each lane replaces its 4 x 4 x 16 values by the products, and the tile is
+// written out by whole rows.
 enum { kEpiPlain = 0, kEpiDa = 1 };
 constexpr int kOutPitch = kT * 2 + 16;
 constexpr int kDgradLds = kLds > kT * kOutPitch ? kLds : kT * kOutPitch;
 
-template <int EPI, int ACT>
+template <int EPI>
 __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                                                  const int32_t* __restrict__ offsets, int E,
                                                  const uint16_t* __restrict__ Bw,
-                                                 const uint16_t* __restrict__ pre,
+                                                 const uint16_t* __restrict__ gp,
                                                  uint16_t* __restrict__ C, int K, int N, int Nt,
                                                  int SBN) {
     __shared__ __attribute__((aligned(1024))) char lds[kDgradLds];
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
             const int r = idx / (kT / 8), c = idx % (kT / 8);
             if (r < rows && c < chunks)
                 *reinterpret_cast<u32x4_t*>(lds + r * kOutPitch + c * 16) =
-                    *reinterpret_cast<const u32x4_t*>(pre + base + (int64_t)r * N + c * 8);
+                    *reinterpret_cast<const u32x4_t*>(gp + base + (int64_t)r * N + c * 8);
         }
         lds_barrier();
     }
@@ -317,10 +319,10 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                               acc[i][j][4 * g + 3]};
                 if constexpr (EPI == kEpiDa) {
                     const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(slot);
-                    v[0] *= activate_grad<ACT>(bf16_lo(pa[0]));
-                    v[1] *= activate_grad<ACT>(bf16_hi(pa[0]));
-                    v[2] *= activate_grad<ACT>(bf16_lo(pa[1]));
-                    v[3] *= activate_grad<ACT>(bf16_hi(pa[1]));
+                    v[0] *= bf16_lo(pa[0]);
+                    v[1] *= bf16_hi(pa[0]);
+                    v[2] *= bf16_lo(pa[1]);
+                    v[3] *= bf16_hi(pa[1]);
                 }
                 u32x2_t o;
                 o[0] = pack_bf16x2(v[0], v[1]);
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
 }  // namespace
 
 hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, const int32_t* offsets,
-                            const void* Bw, const void* pre, void* C, int K, int N,
+                            const void* Bw, const void* gp, void* C, int K, int N,
                             hipStream_t s) {
     const int64_t rows = p.T * p.k;
     const int Mt = (int)((rows + kT - 1) / kT + p.E);          // row tiles, worst case
@@ -403,17 +405,12 @@ hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, cons
     const dim3 grid((unsigned)((int64_t)Mt * Nt)), block(256);
     auto* x = static_cast<const uint16_t*>(X);
     auto* b = static_cast<const uint16_t*>(Bw);
-    auto* pr = static_cast<const uint16_t*>(pre);
+    auto* pr = static_cast<const uint16_t*>(gp);
     auto* c = static_cast<uint16_t*>(C);
-    if (!da)
-        bwd_dgrad<kEpiPlain, kActNone><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
-                                                                  SBN);
-    else if (p.activation == MOE_ACT_SILU)
-        bwd_dgrad<kEpiDa, kActSilu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
-                                                                  SBN);
+    if (da)
+        bwd_dgrad<kEpiDa><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
     else
-        bwd_dgrad<kEpiDa, kActGelu><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt,
-                                                                  SBN);
+        bwd_dgrad<kEpiPlain><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
     return hipGetLastError();
 }
 

@@ -339,53 +339,16 @@ __device__ __forceinline__ void gemm_mainloop(
     wait_vmcnt<0>();
 }
 
-// Bias, activation, bf16 and the store of tile `tr` from the accumulators.
-// One pass of the epilogue: bias and activation A (kActNone: the
-// pre-activation itself) in fp32, one rounding to bf16, the tile staged in LDS
-// and written to out as full rows.  The caller has passed an LDS barrier.
-template <int BM, int A>
-__device__ __forceinline__ void epilogue_pass(const TileRef& tr,
-                                              f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
-                                              char* lds, const uint16_t* __restrict__ be,
-                                              uint16_t* __restrict__ out, int N) {
+// The staged tile (LDS [m][n], pitch Cfg<BM>::OP) to out as full rows.  The
+// caller has passed an LDS barrier after writing it.
+template <int BM>
+__device__ __forceinline__ void store_staged(const TileRef& tr, const char* lds,
+                                             uint16_t* __restrict__ out, int N) {
     using G = Cfg<BM>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % G::WN, wm = wave / G::WN;
-    const int l32 = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < G::FN; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
-            const int n = min(tr.n0 + nl, N - 4);
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (be) {
-                const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(be + n);
-                bv[0] = bf16_lo(bb[0]);
-                bv[1] = bf16_hi(bb[0]);
-                bv[2] = bf16_lo(bb[1]);
-                bv[3] = bf16_hi(bb[1]);
-            }
-#pragma unroll
-            for (int j = 0; j < G::FM; ++j) {
-                const int ml = wm * G::TM + 32 * j + l32;
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    v[q] = activate<A>(acc[i][j][4 * g + q] + bv[q]);
-                }
-                u32x2_t o;
-                o[0] = pack_bf16x2(v[0], v[1]);
-                o[1] = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<u32x2_t*>(lds + ml * G::OP + nl * 2) = o;
-            }
-        }
-    }
-    lds_barrier();
     const int rows = min(G::BM_ROWS, tr.n_rows - tr.m0);
     const int chunks = min(G::BN, N - tr.n0) / 8;         // 16-byte chunks per row (N % 8 == 0)
     uint16_t* cbase = out + (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
-    for (int idx = tid; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
+    for (int idx = threadIdx.x; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
         const int r = idx / (G::BN / 8), c = idx % (G::BN / 8);
         if (r < rows && c < chunks)
             *reinterpret_cast<u32x4_t*>(cbase + (int64_t)r * N + c * 8) =
@@ -398,22 +361,106 @@ __device__ __forceinline__ void epilogue_pass(const TileRef& tr,
 // The tile is staged in LDS ([m][n], 528-byte pitch: the 8-byte writes of 16
 // consecutive rows and the 16-byte reads of one row are both bank-conflict
 // free) and written out as full contiguous row segments, so every 128-byte
-// line of the output is written once.  SAVE: the pre-activation (with bias) is
-// first written to Cpre the same way (kept for the backward).
+// line of the output is written once.  Bias and activation are applied in
+// fp32 with one rounding to bf16.  SAVE (training): the activation's
+// derivative act'(a) at the same fp32 pre-activation, from the same
+// evaluation, is rounded to bf16 and written to Cpre; the backward multiplies
+// by it.  Then the tile goes out in two halves of its rows (each wave's
+// accumulator rows j < FM/2, then the rest), h and act' staged side by side in
+// the same LDS, so both are written as full rows.
 template <int BM, int ACT, bool SAVE>
 __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
                                               f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
                                               char* lds, const uint16_t* __restrict__ bias,
                                               uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
                                               int N) {
+    using G = Cfg<BM>;
     wait_lgkm0();
     lds_barrier();
     const uint16_t* be = bias ? bias + (int64_t)tr.e * N : nullptr;
-    if constexpr (SAVE) {
-        epilogue_pass<BM, kActNone>(tr, acc, lds, be, Cpre, N);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave % G::WN, wm = wave / G::WN;
+    const int l32 = lane & 31, half = lane >> 5;
+    // bias of the lane's columns 32 i + 8 g + 4 half + 0..3
+    auto bias4 = [&](int nl, float (&bv)[4]) {
+        bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
+        if (be) {
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(be + min(tr.n0 + nl, N - 4));
+            bv[0] = bf16_lo(bb[0]);
+            bv[1] = bf16_hi(bb[0]);
+            bv[2] = bf16_lo(bb[1]);
+            bv[3] = bf16_hi(bb[1]);
+        }
+    };
+    if constexpr (!SAVE) {
+#pragma unroll
+        for (int i = 0; i < G::FN; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
+                float bv[4];
+                bias4(nl, bv);
+#pragma unroll
+                for (int j = 0; j < G::FM; ++j) {
+                    const int ml = wm * G::TM + 32 * j + l32;
+                    float v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = activate<ACT>(acc[i][j][4 * g + q] + bv[q]);
+                    const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *reinterpret_cast<u32x2_t*>(lds + ml * G::OP + nl * 2) = o;
+                }
+            }
+        }
         lds_barrier();
+        store_staged<BM>(tr, lds, C, N);
+    } else {
+        constexpr int HJ = G::FM / 2;                  // accumulator rows per half
+        constexpr int HR = G::TM / 2;                  // a wave's rows per half
+        constexpr int HROWS = G::WM * HR;              // staged rows per half
+        constexpr int GOFF = HROWS * G::OP;            // act' region after the h region
+        static_assert(2 * GOFF <= G::LDS_BYTES, "two half tiles fit the staging LDS");
+        const int rows = min(G::BM_ROWS, tr.n_rows - tr.m0);
+        const int chunks = min(G::BN, N - tr.n0) / 8;
+        const int64_t origin = (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            if (hh) lds_barrier();                     // the first half has been copied out
+#pragma unroll
+            for (int i = 0; i < G::FN; ++i) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
+                    float bv[4];
+                    bias4(nl, bv);
+#pragma unroll
+                    for (int jj = 0; jj < HJ; ++jj) {
+                        const int j = hh * HJ + jj;
+                        const int lr = wm * HR + 32 * jj + l32;      // staged row
+                        float v[4], d[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = activate_with_grad<ACT>(acc[i][j][4 * g + q] + bv[q], d[q]);
+                        const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        const u32x2_t gd = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+                        *reinterpret_cast<u32x2_t*>(lds + lr * G::OP + nl * 2) = o;
+                        *reinterpret_cast<u32x2_t*>(lds + GOFF + lr * G::OP + nl * 2) = gd;
+                    }
+                }
+            }
+            lds_barrier();
+            for (int idx = threadIdx.x; idx < HROWS * (G::BN / 8); idx += 256) {
+                const int lr = idx / (G::BN / 8), c = idx % (G::BN / 8);
+                const int r = (lr / HR) * G::TM + hh * HR + lr % HR;  // row of the tile
+                if (r < rows && c < chunks) {
+                    const int64_t at = origin + (int64_t)r * N + c * 8;
+                    *reinterpret_cast<u32x4_t*>(C + at) =
+                        *reinterpret_cast<const u32x4_t*>(lds + lr * G::OP + c * 16);
+                    *reinterpret_cast<u32x4_t*>(Cpre + at) =
+                        *reinterpret_cast<const u32x4_t*>(lds + GOFF + lr * G::OP + c * 16);
+                }
+            }
+        }
     }
-    epilogue_pass<BM, ACT>(tr, acc, lds, be, C, N);
 }
 
 // fp32 partial tile of one K slice, row-major [BM][BN] (Cfg<BM>::UNIT floats
@@ -596,17 +643,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
             }
         }
         float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = a[q] + bv[q];
         const int64_t at = (int64_t)(tr.row_begin + tr.m0 + r) * N + tr.n0 + col;
         u32x2_t w;
-        if (Cpre) {                                       // pre-activation kept for the backward
-            w[0] = pack_bf16x2(o[0], o[1]);
-            w[1] = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<u32x2_t*>(Cpre + at) = w;
-        }
+        if (Cpre) {                                       // act'(a), kept for the backward
+            float d[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(o[q]);
+            for (int q = 0; q < 4; ++q) o[q] = activate_with_grad<ACT>(a[q] + bv[q], d[q]);
+            w[0] = pack_bf16x2(d[0], d[1]);
+            w[1] = pack_bf16x2(d[2], d[3]);
+            *reinterpret_cast<u32x2_t*>(Cpre + at) = w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = activate<ACT>(a[q] + bv[q]);
+        }
         w[0] = pack_bf16x2(o[0], o[1]);
         w[1] = pack_bf16x2(o[2], o[3]);
         *reinterpret_cast<u32x2_t*>(C + at) = w;
@@ -780,11 +829,11 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
 
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         void* hpre, float* part, hipEvent_t mid, hipStream_t s) {
+                         void* hgrad, float* part, hipEvent_t mid, hipStream_t s) {
     if (p.activation == MOE_ACT_SILU)
-        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, hpre, p.H, p.F, part,
+        return launch_gemm<kActSilu>(p, xp, rowmap, offsets, W1, b1, h, hgrad, p.H, p.F, part,
                                      mid, s);
-    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, hpre, p.H, p.F, part, mid,
+    return launch_gemm<kActGelu>(p, xp, rowmap, offsets, W1, b1, h, hgrad, p.H, p.F, part, mid,
                                  s);
 }
 

@@ -162,4 +162,31 @@ __device__ __forceinline__ float activate_grad(float v) {
     else return 1.0f;
 }
 
+// act(a), and act'(a) in g, from one evaluation of the shared terms (the
+// reciprocal, polynomial and exponential of the erf form; the sigmoid).
+template <int ACT>
+__device__ __forceinline__ float activate_with_grad(float a, float& g) {
+    if constexpr (ACT == kActGelu) {
+        const float aa = fabsf(a);
+        const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
+        float poly = fmaf(t, 1.061405429f, -1.453152027f);
+        poly = fmaf(t, poly, 1.421413741f);
+        poly = fmaf(t, poly, -0.284496736f);
+        poly = fmaf(t, poly, 0.254829592f);
+        const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
+        const float q = t * poly * ex;
+        const float Phi = a >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+        g = fmaf(a * 0.39894228040143267794f, ex, Phi);
+        return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
+    } else if constexpr (ACT == kActSilu) {
+        const float s =
+            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
+        g = s * fmaf(a, 1.0f - s, 1.0f);
+        return a * s;
+    } else {
+        g = 1.0f;
+        return a;
+    }
+}
+
 }  // namespace moe

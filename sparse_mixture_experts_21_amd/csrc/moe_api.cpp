@@ -167,12 +167,13 @@ int64_t capacity_of(const moe_problem_t& p) {
 // ---------------------------------------------------------------- training
 // Workspace of moe_forward_train / moe_backward: the forward's layout (whose
 // routing, dispatch, h and y the backward reads) followed by the fp32
-// logits, the pre-activation rows a, and the backward's scratch: dy, dl, da,
+// logits, the rows ga = act'(a) at the first GEMM's pre-activation a, and the
+// backward's scratch: dy, dl, da,
 // dxe (the expert part of dx per kept row), the gathered rows xp and the
 // partial sums of the gate gradients.
 struct TrainLayout {
     WsLayout L;
-    size_t logits, a, dy, dl, da, dxe, xp, gpart, gpb, total;
+    size_t logits, ga, dy, dl, da, dxe, xp, gpart, gpb, total;
 };
 
 TrainLayout train_layout(const moe_problem_t& p) {
@@ -188,7 +189,7 @@ TrainLayout train_layout(const moe_problem_t& p) {
         return o;
     };
     X.logits = take(T * E * 4);
-    X.a = take(T * k * F * 2);
+    X.ga = take(T * k * F * 2);
     X.dy = take(T * k * H * 2);
     X.dl = take(T * E * 4);
     X.da = take(T * k * F * 2);
@@ -211,13 +212,13 @@ moe_status_t check_train(const moe_problem_t* p) {
     return MOE_OK;
 }
 
-// The forward's launch sequence; NULL outputs live in the workspace.  hpre
-// (nullable): also keep the first GEMM's pre-activation rows.
+// The forward's launch sequence; NULL outputs live in the workspace.  hgrad
+// (nullable): also keep act' at the first GEMM's pre-activation rows.
 moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, const void* x,
                           const void* Wg, const void* bg, const void* W1, const void* b1,
                           const void* W2, const void* b2, void* out, float* losses,
                           float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                          int32_t* offsets, int32_t* pos, void* hpre, hipStream_t stream,
+                          int32_t* offsets, int32_t* pos, void* hgrad, hipStream_t stream,
                           hipEvent_t* stage_events) {
     const moe_problem_t* p = &P;
     int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + L.topk_idx);
@@ -244,7 +245,7 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     float* part = reinterpret_cast<float*>(w + L.gemm_part);
     hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
     hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
-    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, hpre, part, up_fix, stream);
+    if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, hgrad, part, up_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
     if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
@@ -495,7 +496,7 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void
     char* w = static_cast<char*>(ws);
     return forward_impl(*p, X.L, w, x, Wg, bg, W1, b1, W2, b2, out, losses,
                         reinterpret_cast<float*>(w + X.logits), nullptr, nullptr, nullptr,
-                        nullptr, nullptr, w + X.a, stream, nullptr);
+                        nullptr, nullptr, w + X.ga, stream, nullptr);
 }
 
 moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg, const void* W1,
@@ -541,7 +542,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg,
     if (e == hipSuccess)
         e = launch_bwd_token(*p, dout, w + L.y, ps, idx, tw, lg, cnt, g_aux, g_z, dy, dl, stream);
     if (e == hipSuccess) e = ev(MOE_BEV_DGRAD_DA);
-    if (e == hipSuccess) e = launch_bwd_dgrad(*p, true, dy, off, W2, w + X.a, da, H, F, stream);
+    if (e == hipSuccess) e = launch_bwd_dgrad(*p, true, dy, off, W2, w + X.ga, da, H, F, stream);
     if (e == hipSuccess) e = ev(MOE_BEV_DGRAD_DXE);
     if (e == hipSuccess) e = launch_bwd_dgrad(*p, false, da, off, W1, nullptr, dxe, F, H, stream);
     if (e == hipSuccess) e = ev(MOE_BEV_DX);

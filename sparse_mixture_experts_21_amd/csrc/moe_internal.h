@@ -79,10 +79,11 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
 // part (nullable): fp32 buffer of gemm_partial_bytes(p) for the K slices of
 // the ragged last round of tiles; without it no tile is cut.
 // mid (nullable): event recorded between the GEMM launch and its fixup.
-// hpre (nullable, bf16 only): also store the pre-activation rows (with bias).
+// hgrad (nullable, bf16 only): also store act'(a) at the pre-activation rows
+// a (with bias), for the backward.
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
-                         void* hpre, float* part, hipEvent_t mid, hipStream_t s);
+                         void* hgrad, float* part, hipEvent_t mid, hipStream_t s);
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
                            hipStream_t s);
@@ -95,9 +96,10 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* 
 hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* pos, void* xp,
                          hipStream_t s);
 // dgrad: C[r][n] = sum_k X[r][k] Bw[e][n][k] over each expert's rows; da: times
-// act'(pre[r][n]).  wgrad: C[e][i][j] = sum over the rows of e of P[r][i] Q[r][j].
+// gp[r][n] (act'(a), saved by the training forward).  wgrad: C[e][i][j] = sum
+// over the rows of e of P[r][i] Q[r][j].
 hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, const int32_t* offsets,
-                            const void* Bw, const void* pre, void* C, int K, int N,
+                            const void* Bw, const void* gp, void* C, int K, int N,
                             hipStream_t s);
 hipError_t launch_bwd_wgrad(const moe_problem_t& p, const void* P, const void* Q,
                             const int32_t* offsets, int I, int J, float* C, hipStream_t s);
