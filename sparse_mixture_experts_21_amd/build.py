@@ -19,8 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "router.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip",
-           "expert_choice.hip", "bwd_gemm.hip", "bwd.hip"]
+SOURCES = ["moe_api.cpp", "router.hip", "dispatch.hip", "route_small.hip", "expert_gemm.hip",
+           "combine.hip", "expert_choice.hip", "bwd_gemm.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for every device pass (the host pass

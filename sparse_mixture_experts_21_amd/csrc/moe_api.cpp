@@ -234,13 +234,21 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
         return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
     };
     hipError_t e = ev(MOE_EV_ROUTE);
-    if (e == hipSuccess)
-        e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, false,
-                         stream);
-    if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
-    if (e == hipSuccess)
-        e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt, losses,
-                           stream);
+    if (route_small_fits(*p)) {
+        // a few tokens: routing and dispatch in one launch (the permute stage is empty)
+        if (e == hipSuccess)
+            e = launch_route_small(*p, capacity_of(*p), x, Wg, bg, logits, idx, tw, cnt, losses,
+                                   off, ps, rt, stream);
+        if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
+    } else {
+        if (e == hipSuccess)
+            e = launch_route(*p, L, w, x, Wg, bg, logits, false, idx, tw, cnt, losses, false,
+                             stream);
+        if (e == hipSuccess) e = ev(MOE_EV_PERMUTE);
+        if (e == hipSuccess)
+            e = launch_permute(*p, L, w, capacity_of(*p), x, idx, off, ps, rt, nullptr, cnt,
+                               losses, stream);
+    }
     if (e == hipSuccess) e = ev(MOE_EV_FFN_UP);
     float* part = reinterpret_cast<float*>(w + L.gemm_part);
     hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;

@@ -74,6 +74,15 @@ hipError_t launch_permute(const moe_problem_t& p, const WsLayout& L, char* ws, i
                           const void* x, const int32_t* topk_idx, int32_t* offsets,
                           int32_t* pos, int32_t* row_token, void* xp, int32_t* fin_counts,
                           float* fin_losses, hipStream_t s);
+// Routing and dispatch of a batch with T * E <= kSmallPairs (bf16) in one
+// launch: what launch_route and launch_permute (with the row gather fused into
+// the first GEMM) produce, in another fixed floating-point order.
+constexpr int kSmallPairs = 64;
+bool route_small_fits(const moe_problem_t& p);
+hipError_t launch_route_small(const moe_problem_t& p, int64_t cap, const void* x, const void* Wg,
+                              const void* bg, float* logits, int32_t* topk_idx, float* topk_w,
+                              int32_t* counts, float* losses, int32_t* offsets, int32_t* pos,
+                              int32_t* row_token, hipStream_t s);
 // rowmap (nullable): when set, row r of the first GEMM reads x[rowmap[r]]
 // instead of xp[r] (the gather fused into the operand load).
 // part (nullable): fp32 buffer of gemm_partial_bytes(p) for the K slices of

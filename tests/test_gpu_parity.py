@@ -70,14 +70,26 @@ SMALL = [
     S("silu_f32_k2_E4_T100_H32_F64", 100, 32, 4, 2, 64, dtype="f32", biases=True, act="silu"),
 ]
 SILU = [s for s in SMALL if s.act == "silu"]
+# Tiny batches (T * E <= 64, bf16): moe_forward routes and dispatches them in
+# one workgroup.  Several LDS blocks of H, a ragged H, a tail block, k = E,
+# E = 1, k = 8 with heavy drops, tied logits, biases, SiLU.
+TINY = [
+    S("tiny_T1_H4096_E8_k2_F512", 1, 4096, 8, 2, 512),
+    S("tiny_T8_H264_E8_k2_F256_cf0.5", 8, 264, 8, 2, 256, cf=0.5, biases=True),
+    S("tiny_T5_H1032_E4_k4_F128", 5, 1032, 4, 4, 128, biases=True),
+    S("tiny_T64_H128_E1_k1_F64", 64, 128, 1, 1, 64),
+    S("tiny_T4_H256_E16_k8_F128_cf0.25", 4, 256, 16, 8, 128, cf=0.25, wg=W.Dist("normal", 0.1)),
+    W.zero_gate(S("tiny_zero_gate_T3_H128_E8_k2_F64_cf0.5", 3, 128, 8, 2, 64, cf=0.5)),
+    S("tiny_silu_T2_H512_E8_k2_F256", 2, 512, 8, 2, 256, act="silu"),
+]
 
 
 def _small_ids():
-    return [s.name for s in SMALL]
+    return [s.name for s in SMALL + TINY]
 
 
 # ---------------------------------------------------------------- end to end (small)
-@pytest.mark.parametrize("spec", SMALL, ids=_small_ids())
+@pytest.mark.parametrize("spec", SMALL + TINY, ids=_small_ids())
 def test_forward_small_all_outputs(spec):
     say(f"[forward small] {spec.name}")
     inp = W.generate(spec)
@@ -119,7 +131,7 @@ def test_stages_equal_forward_bitwise(spec):
     assert torch.equal(xp, ref)
 
 
-@pytest.mark.parametrize("spec", [SMALL[3], SMALL[5], SMALL[7]], ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", [SMALL[3], SMALL[5], SMALL[7], TINY[1]], ids=lambda s: s.name)
 def test_forward_deterministic(spec):
     say(f"[determinism] {spec.name}")
     inp = W.generate(spec)
