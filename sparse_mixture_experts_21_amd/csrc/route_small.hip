@@ -62,21 +62,35 @@ __global__ __launch_bounds__(kSmallThreads) void route_small(
         const int hb = min(HB, H - h0);        // a multiple of 8
         const int nch = hb / 8;
         if (h0) __syncthreads();               // the previous block has been read
-        // x rows: 16-byte vectors
-        for (int i = tid; i < T * nch; i += kSmallThreads) {
-            const int r = i / nch, c = i % nch;
-            *reinterpret_cast<u32x4_t*>(xs + r * PITCH + 8 * c) =
-                *reinterpret_cast<const u32x4_t*>(x + (int64_t)r * H + h0 + 8 * c);
+        // x rows: 16-byte vectors, (row, chunk) pairs dealt to the threads
+        // row-major (the loop is unrolled so several loads are in flight)
+        {
+            const int rpi = max(1, kSmallThreads / nch);          // rows per pass
+            const int r0 = tid / nch, c0 = tid % nch;
+            if (r0 < rpi) {
+#pragma unroll 4
+                for (int r = r0; r < T; r += rpi)
+                    for (int c = c0; c < nch; c += kSmallThreads)
+                        *reinterpret_cast<u32x4_t*>(xs + r * PITCH + 8 * c) =
+                            *reinterpret_cast<const u32x4_t*>(x + (int64_t)r * H + h0 + 8 * c);
+            }
         }
-        // gate rows h0 .. h0 + hb ([hb][E], contiguous): 16-byte vectors,
-        // each element j = hh E + ee scattered to ws[ee][hh]
-        const uint16_t* wsrc = Wg + (int64_t)h0 * E;
-        for (int i = tid; i < hb * E / 8; i += kSmallThreads) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wsrc + 8 * i);
+        // gate row h (E values) by one thread, scattered to ws[e][h]: 16-byte
+        // vectors when E % 8 == 0, else element by element
+#pragma unroll 4
+        for (int hh = tid; hh < hb; hh += kSmallThreads) {
+            const uint16_t* row = Wg + (int64_t)(h0 + hh) * E;
+            if (E % 8 == 0) {
+                for (int e8 = 0; e8 < E; e8 += 8) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + e8);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int j = 8 * i + q, hh = j / E, ee = j % E;
-                ws[ee * PITCH + hh] = (uint16_t)((q & 1) ? (v[q >> 1] >> 16) : (v[q >> 1] & 0xffffu));
+                    for (int q = 0; q < 4; ++q) {
+                        ws[(e8 + 2 * q) * PITCH + hh] = (uint16_t)(v[q] & 0xffffu);
+                        ws[(e8 + 2 * q + 1) * PITCH + hh] = (uint16_t)(v[q] >> 16);
+                    }
+                }
+            } else {
+                for (int ee = 0; ee < E; ++ee) ws[ee * PITCH + hh] = row[ee];
             }
         }
         __syncthreads();
