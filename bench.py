@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: moe_forward_train then moe_backward "
                          "(aux and z loss weights 0.01 and 0.001), one JSON line")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the forward replayed as a captured HIP graph")
     ap.add_argument("--no-abi-timing", action="store_true",
                     help="skip the per-call warm/cold timing that follows the timed steps "
                          "(thousands of extra launches; counter runs of the profiler omit it)")
@@ -487,6 +489,36 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    graph = None
+    if not args.no_graph:
+        # The same forward captured once into a HIP graph and replayed K times:
+        # what a serving loop that replays its layer pays without per-launch
+        # host overhead.  `value` stays the eager rate.
+        log(f"[bench] timing {args.steps} graph replays")
+        ref_out = out.clone()
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            step()
+        gr.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                                ref_out.view(torch.int16) if out.dtype == torch.bfloat16
+                                else ref_out))
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph = {"ms_per_step": gms, "tokens_per_s": T / (gms * 1e-3),
+                 "output_equals_eager": same}
+        del gr
+
     abi, A_abi = None, None
     if not args.no_abi_timing:
         log("[bench] timing each ABI call alone (warm and cold)")
@@ -559,6 +591,7 @@ def main():
                      "traffic": traffic_for(kern, spec.name)},
         "ffn_tflops": ffn_tflops,
         "ffn_frac_of_bf16_peak": ffn_tflops / PEAK_BF16_TFLOPS,
+        "graph": graph,
         "stage_ms": sm,
         "hbm_stages": hbm,
         "abi_ms": abi,
