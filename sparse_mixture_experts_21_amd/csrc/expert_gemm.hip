@@ -31,6 +31,8 @@
 // the CUs, those tiles are cut along K into slices that fill one whole round
 // and write fp32 partials; ffn_gemm_fixup sums them in slice order and applies
 // the epilogue (bias, activation, bf16).
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "lds_dma.h"
 #include "gemm_common.h"
@@ -393,24 +395,32 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
         }
     };
     if constexpr (!SAVE) {
+        // with and without bias (the bias-free layers skip the add)
+        auto stage = [&](auto HB) {
+            constexpr bool kBias = decltype(HB)::value != 0;
 #pragma unroll
-        for (int i = 0; i < G::FN; ++i) {
+            for (int i = 0; i < G::FN; ++i) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
-                float bv[4];
-                bias4(nl, bv);
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * G::TN + 32 * i + 8 * g + 4 * half;
+                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (kBias) bias4(nl, bv);
 #pragma unroll
-                for (int j = 0; j < G::FM; ++j) {
-                    const int ml = wm * G::TM + 32 * j + l32;
-                    float v[4];
+                    for (int j = 0; j < G::FM; ++j) {
+                        const int ml = wm * G::TM + 32 * j + l32;
+                        float v[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = activate<ACT>(acc[i][j][4 * g + q] + bv[q]);
-                    const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                    *reinterpret_cast<u32x2_t*>(lds + ml * G::OP + nl * 2) = o;
+                        for (int q = 0; q < 4; ++q)
+                            v[q] = activate<ACT>(kBias ? acc[i][j][4 * g + q] + bv[q]
+                                                       : acc[i][j][4 * g + q]);
+                        const u32x2_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        *reinterpret_cast<u32x2_t*>(lds + ml * G::OP + nl * 2) = o;
+                    }
                 }
             }
-        }
+        };
+        if (be) stage(std::integral_constant<int, 1>{});
+        else stage(std::integral_constant<int, 0>{});
         lds_barrier();
         store_staged<BM>(tr, lds, C, N);
     } else {

@@ -18,16 +18,21 @@ enum Act { kActNone = 0, kActGelu = 1, kActSilu = 2 };
 // i.e. below fp32 rounding of GELU's output scale and far below bf16.  With
 // u = |a| / sqrt 2 the factor 1/sqrt 2 folds into p, and exp(-u^2) is
 // 2^(a^2 * (-1 / (2 ln 2))).  One reciprocal and one exponential, no branches.
+// The coefficients are halved (exactly: a power of two), so the polynomial
+// gives h = q / 2 directly.
+__device__ __forceinline__ float gelu_half_q(float a, float& ex) {
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, fabsf(a), 1.0f));
+    float poly = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+    poly = fmaf(t, poly, 0.5f * 1.421413741f);
+    poly = fmaf(t, poly, 0.5f * -0.284496736f);
+    poly = fmaf(t, poly, 0.5f * 0.254829592f);
+    ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
+    return t * poly * ex;                                 // (1 - erf(|a| / sqrt 2)) / 2
+}
 __device__ __forceinline__ float gelu_erf(float a) {
-    const float aa = fabsf(a);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
-    const float q = t * poly * ex;                        // 1 - erf(|a| / sqrt 2)
-    return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
+    float ex;
+    const float h = gelu_half_q(a, ex);
+    return fmaf(-fabsf(a), h, fmaxf(a, 0.0f));
 }
 
 // SiLU, a * sigmoid(a) = a / (1 + e^-a) with e^-a = 2^(-a log2 e).  For very
@@ -137,15 +142,9 @@ __device__ __forceinline__ int real_row_tiles(const int32_t* __restrict__ offset
 // gelu_erf, Phi(a) = 1 - q/2 for a >= 0 and q/2 below, and phi(a) =
 // exp(-a^2 / 2) / sqrt(2 pi) is the same exponential times 1 / sqrt(2 pi).
 __device__ __forceinline__ float gelu_erf_grad(float a) {
-    const float aa = fabsf(a);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
-    const float q = t * poly * ex;
-    const float Phi = a >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+    float ex;
+    const float h = gelu_half_q(a, ex);                   // q / 2
+    const float Phi = a >= 0.0f ? 1.0f - h : h;
     return fmaf(a * 0.39894228040143267794f, ex, Phi);
 }
 
@@ -167,17 +166,10 @@ __device__ __forceinline__ float activate_grad(float v) {
 template <int ACT>
 __device__ __forceinline__ float activate_with_grad(float a, float& g) {
     if constexpr (ACT == kActGelu) {
-        const float aa = fabsf(a);
-        const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752440f, aa, 1.0f));
-        float poly = fmaf(t, 1.061405429f, -1.453152027f);
-        poly = fmaf(t, poly, 1.421413741f);
-        poly = fmaf(t, poly, -0.284496736f);
-        poly = fmaf(t, poly, 0.254829592f);
-        const float ex = __builtin_amdgcn_exp2f(a * (a * -0.72134752044448170368f));
-        const float q = t * poly * ex;
-        const float Phi = a >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
-        g = fmaf(a * 0.39894228040143267794f, ex, Phi);
-        return fmaf(-0.5f * aa, q, fmaxf(a, 0.0f));
+        float ex;
+        const float h = gelu_half_q(a, ex);               // q / 2
+        g = fmaf(a * 0.39894228040143267794f, ex, a >= 0.0f ? 1.0f - h : h);
+        return fmaf(-fabsf(a), h, fmaxf(a, 0.0f));
     } else if constexpr (ACT == kActSilu) {
         const float s =
             __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * -1.44269504088896340736f));
