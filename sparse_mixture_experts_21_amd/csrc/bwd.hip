@@ -175,46 +175,68 @@ __global__ __launch_bounds__(256) void bwd_colsum(const uint16_t* __restrict__ r
 
 // dWg partials: workgroup (block of 512 hidden units, token chunk c, expert
 // block of kGateE): part[c][h][e] = sum over the chunk's tokens (ascending) of
-// x[t][h] dl[t][e], two hidden units per thread; the x values of 8 tokens are
-// loaded before their products are added.  The first hidden-unit block also
-// writes pb[c][e] = sum of dl[t][e] over the chunk.
+// x[t][h] dl[t][e], two hidden units per thread.  The chunk's dl rows go
+// through LDS in sub-blocks of kGateSub tokens, padded with zeros past the
+// last token and the last expert, so the products run with fixed trip counts
+// and no branches (the padding adds exact zeros); each thread loads the x
+// values of kGateTok tokens before adding their products.  The first
+// hidden-unit block also writes pb[c][e] = sum of dl[t][e] over the chunk.
 constexpr int kGateE = 16;
-constexpr int kGateTok = 8;
+constexpr int kGateTok = 16;
+constexpr int kGateSub = 128;               // tokens per LDS sub-block
+constexpr int kGateMaxChunks = 1024;
 
 __global__ __launch_bounds__(256) void bwd_gate_partial(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ dl, int64_t T,
                                                         int H, int E, int64_t chunk,
                                                         float* __restrict__ part,
                                                         float* __restrict__ pb) {
-    const int h = 2 * (blockIdx.x * 256 + threadIdx.x);     // H % 8 == 0: h + 1 < H with h
+    __shared__ __attribute__((aligned(16))) float sdl[kGateSub][kGateE];
+    const int tid = threadIdx.x;
+    const int h = 2 * (blockIdx.x * 256 + tid);            // H % 8 == 0: h + 1 < H with h
+    const bool hv = h < H;
     const int c = blockIdx.y, e0 = blockIdx.z * kGateE;
     const int ne = min(kGateE, E - e0);
     const int64_t t0 = (int64_t)c * chunk, t1 = min(t0 + chunk, T);
-    float acc0[kGateE], acc1[kGateE];
+    float acc0[kGateE], acc1[kGateE], bsum = 0.f;
 #pragma unroll
     for (int j = 0; j < kGateE; ++j) acc0[j] = acc1[j] = 0.f;
-    if (h < H) {
-        for (int64_t tb = t0; tb < t1; tb += kGateTok) {
+    for (int64_t sb = t0; sb < t1; sb += kGateSub) {
+        const int n = (int)min<int64_t>(kGateSub, t1 - sb);
+        __syncthreads();                                   // the previous sub-block is read
+        for (int i = tid; i < kGateSub * kGateE; i += 256) {
+            const int r = i / kGateE, j = i % kGateE;
+            sdl[r][j] = (r < n && j < ne) ? dl[(sb + r) * E + e0 + j] : 0.f;
+        }
+        __syncthreads();
+        // bias gradient: thread j < ne of the first hidden-unit block sums column j
+        if (blockIdx.x == 0 && tid < ne)
+            for (int r = 0; r < n; ++r) bsum += sdl[r][tid];
+        for (int tb = 0; tb < kGateSub; tb += kGateTok) {
             uint32_t xv[kGateTok];
 #pragma unroll
             for (int u = 0; u < kGateTok; ++u) {
-                const int64_t t = min(tb + u, t1 - 1);       // clamped, masked below
-                xv[u] = *reinterpret_cast<const uint32_t*>(x + t * H + h);
+                // rows past the chunk read its last row; their dl is zero
+                const int64_t t = sb + min(tb + u, n - 1);
+                xv[u] = hv ? *reinterpret_cast<const uint32_t*>(x + t * H + h) : 0u;
             }
 #pragma unroll
             for (int u = 0; u < kGateTok; ++u) {
-                if (tb + u >= t1) break;
-                const float* d = dl + (tb + u) * E + e0;
                 const float x0 = bf16_lo(xv[u]), x1 = bf16_hi(xv[u]);
+                const f32x4_t* d = reinterpret_cast<const f32x4_t*>(sdl[tb + u]);
 #pragma unroll
-                for (int j = 0; j < kGateE; ++j) {
-                    if (j < ne) {
-                        acc0[j] = fmaf(x0, d[j], acc0[j]);
-                        acc1[j] = fmaf(x1, d[j], acc1[j]);
+                for (int q = 0; q < kGateE / 4; ++q) {
+                    const f32x4_t dv = d[q];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc0[4 * q + r] = fmaf(x0, dv[r], acc0[4 * q + r]);
+                        acc1[4 * q + r] = fmaf(x1, dv[r], acc1[4 * q + r]);
                     }
                 }
             }
         }
+    }
+    if (hv) {
         float* o = part + ((int64_t)c * H + h) * E + e0;
 #pragma unroll
         for (int j = 0; j < kGateE; ++j)
@@ -223,18 +245,9 @@ __global__ __launch_bounds__(256) void bwd_gate_partial(const uint16_t* __restri
                 o[E + j] = acc1[j];
             }
     }
-    if (blockIdx.x == 0) {                                // uniform over the workgroup
-        __shared__ float red[256 / 64];
-        for (int j = 0; j < ne; ++j) {
-            float b = 0.f;
-            for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) b += dl[t * E + e0 + j];
-            b = block_sum(b, red);
-            if (threadIdx.x == 0) pb[(int64_t)c * E + e0 + j] = b;
-        }
-    }
+    if (blockIdx.x == 0 && tid < ne) pb[(int64_t)c * E + e0 + tid] = bsum;
 }
 
-// dWg[h][e] = sum over chunks (in order) of part; dbg[e] likewise from pb.
 __global__ __launch_bounds__(256) void bwd_gate_reduce(const float* __restrict__ part,
                                                        const float* __restrict__ pb, int H, int E,
                                                        int nchunk, float* __restrict__ dWg,
@@ -254,7 +267,9 @@ __global__ __launch_bounds__(256) void bwd_gate_reduce(const float* __restrict__
 
 }  // namespace
 
-int64_t bwd_gate_chunks(const moe_problem_t& p) { return std::min<int64_t>(64, (p.T + 255) / 256); }
+int64_t bwd_gate_chunks(const moe_problem_t& p) {
+    return std::min<int64_t>(kGateMaxChunks, (p.T + kGateSub - 1) / kGateSub);
+}
 
 hipError_t launch_bwd_token(const moe_problem_t& p, const void* dout, const void* y,
                             const int32_t* pos, const int32_t* topk_idx, const float* topk_w,
