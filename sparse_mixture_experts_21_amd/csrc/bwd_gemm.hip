@@ -250,10 +250,10 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
 // straddling experts) x a column tile, in the forward GEMM's tile order.
 // EPI_DA: multiply by gp[r][n] = act'(a[r][n]), saved by the training
 // forward's first GEMM; EPI_PLAIN: store as is.  Output bf16 [rows][N].
-// The epilogue works on the tile in LDS ([m][n] bf16, 528-byte pitch, as the
-// forward's): with EPI_DA the act' tile is first loaded there by whole rows,
-// each lane replaces its 4 x 4 x 16 values by the products, and the tile is
-// written out by whole rows.
+// The epilogue stages the tile in LDS ([m][n] bf16, 528-byte pitch, as the
+// forward's) and writes it out by whole rows; with EPI_DA each lane first
+// multiplies its values by the act' values at the same positions, loaded
+// straight from global memory (8 bytes per lane and accumulator row).
 enum { kEpiPlain = 0, kEpiDa = 1 };
 constexpr int kOutPitch = kT * 2 + 16;
 constexpr int kDgradLds = kLds > kT * kOutPitch ? kLds : kT * kOutPitch;
@@ -297,15 +297,7 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
     const int chunks = min(kT, N - n0) / 8;             // 16-byte chunks per row (N % 8 == 0)
     const int64_t base = (int64_t)(row_begin + m0) * N + n0;
     lds_barrier();
-    if constexpr (EPI == kEpiDa) {
-        for (int idx = tid; idx < kT * (kT / 8); idx += 256) {
-            const int r = idx / (kT / 8), c = idx % (kT / 8);
-            if (r < rows && c < chunks)
-                *reinterpret_cast<u32x4_t*>(lds + r * kOutPitch + c * 16) =
-                    *reinterpret_cast<const u32x4_t*>(gp + base + (int64_t)r * N + c * 8);
-        }
-        lds_barrier();
-    }
+    const int cols = min(kT, N - n0);
 #pragma unroll
     for (int j = 0; j < kF; ++j) {
         const int m = 128 * wm + 32 * j + l32;
@@ -318,7 +310,10 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
                 float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                               acc[i][j][4 * g + 3]};
                 if constexpr (EPI == kEpiDa) {
-                    const u32x2_t pa = *reinterpret_cast<const u32x2_t*>(slot);
+                    // the lane's own 4 act' values, straight from global memory
+                    u32x2_t pa = {0u, 0u};
+                    if (m < rows && nl < cols)
+                        pa = *reinterpret_cast<const u32x2_t*>(gp + base + (int64_t)m * N + nl);
                     v[0] *= bf16_lo(pa[0]);
                     v[1] *= bf16_hi(pa[0]);
                     v[2] *= bf16_lo(pa[1]);
