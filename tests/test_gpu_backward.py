@@ -49,6 +49,8 @@ SMALL = [
     S("bwd_ragged_T777_H264_E6_k2_F776_cf1.25", 777, 264, 6, 2, 776, cf=1.25, biases=True),
     S("bwd_k1_T300_H128_E4_k1_F384", 300, 128, 4, 1, 384),
     S("bwd_E32_T1000_H128_E32_k3_F256_cf0.5", 1000, 128, 32, 3, 256, cf=0.5),
+    # a tiny batch: the training forward routes and dispatches it in one launch
+    S("bwd_tiny_T6_H256_E8_k2_F512_cf0.5", 6, 256, 8, 2, 512, cf=0.5, biases=True),
 ]
 GAUX, GZ = 0.05, 0.01
 
