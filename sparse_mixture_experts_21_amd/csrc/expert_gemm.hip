@@ -15,7 +15,8 @@
 // synchronisation is needed; surplus workgroups return at once and experts
 // with no rows cost nothing (their weights are never read).
 //
-// bf16 kernel (gfx950): 256 threads, tile BN = 256 output columns x BM rows,
+// bf16 kernel (gfx950): 256 threads (512 for the 256-row tile of the GEMM
+// with an activation: 2 waves per SIMD), tile BN = 256 output columns x BM rows,
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, issued as
 // D[n][m] = W^T[n][k] . X^T[k][m] so each lane of the epilogue owns 4
 // consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
