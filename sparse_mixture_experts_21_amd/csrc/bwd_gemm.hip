@@ -28,25 +28,38 @@ namespace moe {
 namespace {
 
 constexpr int kT = 256;                 // tile edge (both output dimensions)
-constexpr int kF = 4;                   // 32 x 32 MFMA tiles per wave and dimension
+constexpr int kF = 4;                   // 32 x 32 MFMA tiles per wave and dimension (4 waves)
 constexpr int kLds = 128 * 1024;        // the DMA ring: 2 stages of 64-deep or 4 of 32-deep k-tiles
 
 // k-tile depth BK and what follows from it: LDS stages, bytes of one operand
-// tile per stage, 1 KB DMA blocks per wave per operand, and the row layout's
-// 16-byte chunks per row, rows per 1 KB block and swizzle shift.
+// tile per stage, and the row layout's 16-byte chunks per row, rows per 1 KB
+// block and swizzle shift.
 template <int BK_>
 struct KT {
     static constexpr int BK = BK_;
     static constexpr int NS = BK == 64 ? 2 : 4;
     static constexpr int OP = kT * BK * 2;
     static constexpr int STAGE = 2 * OP;
-    static constexpr int DMA = OP / 4096;
     static constexpr int CPR = BK / 8, RPB = 64 / CPR, RSH = CPR == 4 ? 2 : 1;
     static_assert(BK == 32 || BK == 64, "k-tile depth");
     static_assert(NS * STAGE == kLds, "ring size");
 };
 
 enum Layout { kRow = 0, kKmaj = 1 };
+
+// Waves of a workgroup over the 256 x 256 tile: 2 along the output rows (B
+// side) and NW / 2 along the output columns (A side).  4 waves: 128 x 128 per
+// wave; 8 waves (2 per SIMD): 128 rows x 64 columns per wave.
+template <int NW_>
+struct WaveLayout {
+    static constexpr int NW = NW_;
+    static constexpr int WN = NW / 2;                  // waves along the columns
+    static constexpr int TA = kT / WN, TB = kT / 2;    // per-wave extent: columns, rows
+    static constexpr int FA = TA / 32, FB = TB / 32;   // 32 x 32 MFMA tiles per wave
+    static_assert(NW == 4 || NW == 8, "waves");
+};
+template <int NW>
+using BAcc = f32x16_t[WaveLayout<NW>::FA][WaveLayout<NW>::FB];
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -65,10 +78,10 @@ struct Operand {
 
 // Byte offset (within the operand's resource) of DMA q's 16 bytes for k-tile
 // t, and the LDS byte offset it lands at, for this lane.
-template <int L, class Q>
+template <int L, class Q, int NW>
 __device__ __forceinline__ uint32_t dma_src(const Operand& o, int q, int t) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int blk = 4 * q + wave;                       // 1 KB block of the stage tile
+    const int blk = NW * q + wave;                      // 1 KB block of the stage tile
     if constexpr (L == kRow) {
         // RPB rows of 2 BK bytes per block; chunk c of row idx stored at
         // c ^ ((idx >> RSH) % CPR)
@@ -127,52 +140,56 @@ __device__ __forceinline__ bf16x8_t read_frag(uint32_t a) {
 // H2 in the next substep), and the fragments of the next substep are read
 // between the current substep's MFMAs (scheduling groups), with one barrier
 // per k-tile.
-template <int LA, int LB, int BK>
+template <int LA, int LB, int BK, int NW>
 __device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B, int nk,
-                                             char* lds, f32x16_t (&acc)[kF][kF]) {
+                                             char* lds, BAcc<NW>& acc) {
     using Q = KT<BK>;
-    constexpr int kNS = Q::NS, kStage = Q::STAGE, kOpBytes = Q::OP, kDmaPerOp = Q::DMA;
+    using WL = WaveLayout<NW>;
+    constexpr int FA = WL::FA, FB = WL::FB;
+    constexpr int kNS = Q::NS, kStage = Q::STAGE, kOpBytes = Q::OP;
+    constexpr int kDmaPerOp = kOpBytes / (1024 * NW);  // 1 KB DMA blocks per wave per operand
+    static_assert(kDmaPerOp * 1024 * NW == kOpBytes, "operand tile splits over the waves");
     const int wave = threadIdx.x >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WL::WN, wm = wave / WL::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
     constexpr int NDMA = 2 * kDmaPerOp;
     auto issue_one = [&](int t, int q) {
         const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
         if (q < kDmaPerOp) {
-            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024));
-            dma16(A.rsrc, dma_src<LA, Q>(A, q, t), l);
+            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((NW * q + wave) * 1024));
+            dma16(A.rsrc, dma_src<LA, Q, NW>(A, q, t), l);
         } else {
             const int qb = q - kDmaPerOp;
             const uint32_t l = __builtin_amdgcn_readfirstlane(
-                st + (uint32_t)(kOpBytes + (4 * qb + wave) * 1024));
-            dma16(B.rsrc, dma_src<LB, Q>(B, qb, t), l);
+                st + (uint32_t)(kOpBytes + (NW * qb + wave) * 1024));
+            dma16(B.rsrc, dma_src<LB, Q, NW>(B, qb, t), l);
         }
     };
-    bf16x8_t fa[2][kF], fb[2][kF];
-    // fragment f (f < kF: A side, else B side) of substep kk of k-tile t
+    bf16x8_t fa[2][FA], fb[2][FB];
+    // fragment f (f < FA: A side, else B side) of substep kk of k-tile t
     auto read_one = [&](int t, int kk, int buf, int f) {
         const uint32_t st = lds0 + (uint32_t)((t % kNS) * kStage);
-        if (f < kF) fa[buf][f] = read_frag<LA>(st + frag_addr<LA, Q>(128 * wn, f, kk));
-        else fb[buf][f - kF] = read_frag<LB>(st + kOpBytes + frag_addr<LB, Q>(128 * wm, f - kF, kk));
+        if (f < FA) fa[buf][f] = read_frag<LA>(st + frag_addr<LA, Q>(WL::TA * wn, f, kk));
+        else fb[buf][f - FA] = read_frag<LB>(st + kOpBytes + frag_addr<LB, Q>(WL::TB * wm, f - FA, kk));
     };
-    // fragments in the order the MFMAs consume them: A0, B0..B3, A1..A3
-    auto frag_id = [](int o) { return o == 0 ? 0 : (o <= kF ? kF + o - 1 : o - kF); };
+    // fragments in the order the MFMAs consume them: A0, B0..B(FB-1), A1..
+    auto frag_id = [](int o) { return o == 0 ? 0 : (o <= FB ? FA + o - 1 : o - FB); };
     auto read_all = [&](int t, int kk, int buf) {
 #pragma unroll
-        for (int o = 0; o < 2 * kF; ++o) read_one(t, kk, buf, frag_id(o));
+        for (int o = 0; o < FA + FB; ++o) read_one(t, kk, buf, frag_id(o));
     };
     auto mfma_range = [&](int buf, int lo, int hi) {
 #pragma unroll
-        for (int x = 0; x < kF * kF; ++x) {
+        for (int x = 0; x < FA * FB; ++x) {
             if (x < lo || x >= hi) continue;
-            const int i = x / kF, j = x % kF;
+            const int i = x / FB, j = x % FB;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],
                                                                 acc[i][j], 0, 0, 0);
         }
     };
-    constexpr int NMF = kF * kF;
-    constexpr int NRD = (LA == kKmaj ? 2 : 1) * kF + (LB == kKmaj ? 2 : 1) * kF;
-    constexpr int NF = 2 * kF;
+    constexpr int NMF = FA * FB;
+    constexpr int NRD = (LA == kKmaj ? 2 : 1) * FA + (LB == kKmaj ? 2 : 1) * FB;
+    constexpr int NF = FA + FB;
     constexpr int H1 = (NDMA + 1) / 2, H2 = NDMA - H1;
     constexpr int NSUB = BK / 16;
     constexpr int RG2 = H2 > 1 ? H2 / 2 : 1, RG1 = H1 > 1 ? H1 / 2 : 1;
@@ -243,11 +260,12 @@ __device__ __forceinline__ void bwd_mainloop(const Operand& A, const Operand& B,
     wait_lgkm0();
 }
 
-__device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
+template <int NW>
+__device__ __forceinline__ void zero(BAcc<NW>& acc) {
 #pragma unroll
-    for (int i = 0; i < kF; ++i)
+    for (int i = 0; i < WaveLayout<NW>::FA; ++i)
 #pragma unroll
-        for (int j = 0; j < kF; ++j)
+        for (int j = 0; j < WaveLayout<NW>::FB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
@@ -261,12 +279,16 @@ __device__ __forceinline__ void zero(f32x16_t (&acc)[kF][kF]) {
 // forward's) and writes it out by whole rows; with EPI_DA each lane first
 // multiplies its values by the act' values at the same positions, loaded
 // straight from global memory (8 bytes per lane and accumulator row).
+// EPI_DA runs 8 waves (2 per SIMD), so one wave's MFMAs cover the other's
+// LDS reads; the plain dgrad keeps 4.
 enum { kEpiPlain = 0, kEpiDa = 1 };
+template <int EPI>
+constexpr int dgrad_waves() { return EPI == kEpiDa ? 8 : 4; }
 constexpr int kOutPitch = kT * 2 + 16;
 constexpr int kDgradLds = kLds > kT * kOutPitch ? kLds : kT * kOutPitch;
 
 template <int EPI>
-__global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(64 * dgrad_waves<EPI>()) void bwd_dgrad(const uint16_t* __restrict__ X,
                                                  const int32_t* __restrict__ offsets, int E,
                                                  const uint16_t* __restrict__ Bw,
                                                  const uint16_t* __restrict__ gp,
@@ -294,26 +316,28 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
     b.ld = (uint32_t)K * 2u;
     b.n_idx = rows;
     b.n_k = K;
-    f32x16_t acc[kF][kF];
-    zero(acc);
+    constexpr int NW = dgrad_waves<EPI>();
+    using WL = WaveLayout<NW>;
+    BAcc<NW> acc;
+    zero<NW>(acc);
     // dgrad: 64-deep k-tiles in 2 stages
-    bwd_mainloop<kRow, kRow, 64>(a, b, (K + 63) / 64, lds, acc);
+    bwd_mainloop<kRow, kRow, 64, NW>(a, b, (K + 63) / 64, lds, acc);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WL::WN, wm = wave / WL::WN;
     const int l32 = lane & 31, half = lane >> 5;
     const int chunks = min(kT, N - n0) / 8;             // 16-byte chunks per row (N % 8 == 0)
     const int64_t base = (int64_t)(row_begin + m0) * N + n0;
     lds_barrier();
     const int cols = min(kT, N - n0);
 #pragma unroll
-    for (int j = 0; j < kF; ++j) {
-        const int m = 128 * wm + 32 * j + l32;
+    for (int j = 0; j < WL::FB; ++j) {
+        const int m = WL::TB * wm + 32 * j + l32;
 #pragma unroll
-        for (int i = 0; i < kF; ++i)
+        for (int i = 0; i < WL::FA; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int nl = 128 * wn + 32 * i + 8 * g + 4 * half;
+                const int nl = WL::TA * wn + 32 * i + 8 * g + 4 * half;
                 char* slot = lds + m * kOutPitch + nl * 2;
                 float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                               acc[i][j][4 * g + 3]};
@@ -334,7 +358,7 @@ __global__ __launch_bounds__(256) void bwd_dgrad(const uint16_t* __restrict__ X,
             }
     }
     lds_barrier();
-    for (int idx = tid; idx < kT * (kT / 8); idx += 256) {
+    for (int idx = tid; idx < kT * (kT / 8); idx += 64 * NW) {
         const int r = idx / (kT / 8), c = idx % (kT / 8);
         if (r < rows && c < chunks)
             *reinterpret_cast<u32x4_t*>(C + base + (int64_t)r * N + c * 8) =
@@ -371,10 +395,10 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
     b.ld = (uint32_t)I * 2u;
     b.n_idx = min(kT, I - i0);
     b.n_k = nr;
-    f32x16_t acc[kF][kF];
-    zero(acc);
+    BAcc<4> acc;
+    zero<4>(acc);
     // wgrad: 32-deep k-tiles in 4 stages (measured a little faster here)
-    bwd_mainloop<kKmaj, kKmaj, 32>(a, b, (nr + 31) / 32, lds, acc);
+    bwd_mainloop<kKmaj, kKmaj, 32, 4>(a, b, (nr + 31) / 32, lds, acc);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave & 1, wm = wave >> 1;
@@ -406,15 +430,17 @@ hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, cons
     const int Mt = (int)((rows + kT - 1) / kT + p.E);          // row tiles, worst case
     const int Nt = (N + kT - 1) / kT;
     const int SBN = (Nt % 16 == 0) ? 16 : (Nt % 8 == 0) ? 8 : 4;
-    const dim3 grid((unsigned)((int64_t)Mt * Nt)), block(256);
+    const dim3 grid((unsigned)((int64_t)Mt * Nt));
     auto* x = static_cast<const uint16_t*>(X);
     auto* b = static_cast<const uint16_t*>(Bw);
     auto* pr = static_cast<const uint16_t*>(gp);
     auto* c = static_cast<uint16_t*>(C);
     if (da)
-        bwd_dgrad<kEpiDa><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
+        bwd_dgrad<kEpiDa><<<grid, dim3(64 * dgrad_waves<kEpiDa>()), 0, s>>>(x, offsets, p.E, b, pr,
+                                                                            c, K, N, Nt, SBN);
     else
-        bwd_dgrad<kEpiPlain><<<grid, block, 0, s>>>(x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
+        bwd_dgrad<kEpiPlain><<<grid, dim3(64 * dgrad_waves<kEpiPlain>()), 0, s>>>(
+            x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
     return hipGetLastError();
 }
 
