@@ -9,8 +9,9 @@
 //   wgrad   C[e][i][j] = sum_r P[r][i] Q[r][j]       both operands row-major over r
 //           (dW2[e] = h^T dy:  P = h, Q = dy;  dW1[e] = xp^T da:  P = xp, Q = da)
 //
-// The tile machinery is the forward's: 256 x 256 output tiles, 4 waves of
-// 128 x 128 on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, operands moved
+// The tile machinery is the forward's: 256 x 256 output tiles, 8 waves (2 per
+// SIMD) of 128 rows x 64 columns on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation, operands moved
 // HBM -> LDS by buffer_load ... lds through a 128 KB ring (dgrad: 2 stages of
 // 64-deep k-tiles; wgrad: 4 stages of 32-deep ones).  An
 // operand is either K-contiguous ("row" layout: LDS [idx][k], 64-byte rows,
@@ -28,7 +29,6 @@ namespace moe {
 namespace {
 
 constexpr int kT = 256;                 // tile edge (both output dimensions)
-constexpr int kF = 4;                   // 32 x 32 MFMA tiles per wave and dimension (4 waves)
 constexpr int kLds = 128 * 1024;        // the DMA ring: 2 stages of 64-deep or 4 of 32-deep k-tiles
 
 // k-tile depth BK and what follows from it: LDS stages, bytes of one operand
@@ -279,16 +279,15 @@ __device__ __forceinline__ void zero(BAcc<NW>& acc) {
 // forward's) and writes it out by whole rows; with EPI_DA each lane first
 // multiplies its values by the act' values at the same positions, loaded
 // straight from global memory (8 bytes per lane and accumulator row).
-// EPI_DA runs 8 waves (2 per SIMD), so one wave's MFMAs cover the other's
-// LDS reads; the plain dgrad keeps 4.
+// Both run 8 waves (2 per SIMD, 128 x 64 each), so one wave's MFMAs cover
+// the other's LDS reads.
 enum { kEpiPlain = 0, kEpiDa = 1 };
-template <int EPI>
-constexpr int dgrad_waves() { return EPI == kEpiDa ? 8 : 4; }
+constexpr int kBwdWaves = 8;
 constexpr int kOutPitch = kT * 2 + 16;
 constexpr int kDgradLds = kLds > kT * kOutPitch ? kLds : kT * kOutPitch;
 
 template <int EPI>
-__global__ __launch_bounds__(64 * dgrad_waves<EPI>()) void bwd_dgrad(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_dgrad(const uint16_t* __restrict__ X,
                                                  const int32_t* __restrict__ offsets, int E,
                                                  const uint16_t* __restrict__ Bw,
                                                  const uint16_t* __restrict__ gp,
@@ -316,7 +315,7 @@ __global__ __launch_bounds__(64 * dgrad_waves<EPI>()) void bwd_dgrad(const uint1
     b.ld = (uint32_t)K * 2u;
     b.n_idx = rows;
     b.n_k = K;
-    constexpr int NW = dgrad_waves<EPI>();
+    constexpr int NW = kBwdWaves;
     using WL = WaveLayout<NW>;
     BAcc<NW> acc;
     zero<NW>(acc);
@@ -370,7 +369,7 @@ __global__ __launch_bounds__(64 * dgrad_waves<EPI>()) void bwd_dgrad(const uint1
 // Workgroup p: expert p / (It Jt), output tile (i, j) of C[e] [I][J] (fp32):
 // C[e][i][j] = sum over the expert's rows r of P[r][i] Q[r][j].  An expert
 // without rows gets zeros.
-__global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
+__global__ __launch_bounds__(64 * kBwdWaves) void bwd_wgrad(const uint16_t* __restrict__ P,
                                                  const uint16_t* __restrict__ Q,
                                                  const int32_t* __restrict__ offsets, int I,
                                                  int J, int It, int Jt, int E, int SBN,
@@ -395,24 +394,24 @@ __global__ __launch_bounds__(256) void bwd_wgrad(const uint16_t* __restrict__ P,
     b.ld = (uint32_t)I * 2u;
     b.n_idx = min(kT, I - i0);
     b.n_k = nr;
-    BAcc<4> acc;
-    zero<4>(acc);
+    BAcc<kBwdWaves> acc;
+    zero<kBwdWaves>(acc);
     // wgrad: 32-deep k-tiles in 4 stages (measured a little faster here)
-    bwd_mainloop<kKmaj, kKmaj, 32, 4>(a, b, (nr + 31) / 32, lds, acc);
-
+    bwd_mainloop<kKmaj, kKmaj, 32, kBwdWaves>(a, b, (nr + 31) / 32, lds, acc);
+    using WL = WaveLayout<kBwdWaves>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WL::WN, wm = wave / WL::WN;
     const int l32 = lane & 31, half = lane >> 5;
     float* Ce = C + (int64_t)e * I * J;
 #pragma unroll
-    for (int jj = 0; jj < kF; ++jj) {
-        const int i = i0 + 128 * wm + 32 * jj + l32;
+    for (int jj = 0; jj < WL::FB; ++jj) {
+        const int i = i0 + WL::TB * wm + 32 * jj + l32;
         if (i >= I) continue;
 #pragma unroll
-        for (int ii = 0; ii < kF; ++ii)
+        for (int ii = 0; ii < WL::FA; ++ii)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int j = j0 + 128 * wn + 32 * ii + 8 * g + 4 * half;
+                const int j = j0 + WL::TA * wn + 32 * ii + 8 * g + 4 * half;
                 if (j >= J) continue;
                 const f32x4_t v = {acc[ii][jj][4 * g], acc[ii][jj][4 * g + 1],
                                    acc[ii][jj][4 * g + 2], acc[ii][jj][4 * g + 3]};
@@ -436,11 +435,11 @@ hipError_t launch_bwd_dgrad(const moe_problem_t& p, bool da, const void* X, cons
     auto* pr = static_cast<const uint16_t*>(gp);
     auto* c = static_cast<uint16_t*>(C);
     if (da)
-        bwd_dgrad<kEpiDa><<<grid, dim3(64 * dgrad_waves<kEpiDa>()), 0, s>>>(x, offsets, p.E, b, pr,
-                                                                            c, K, N, Nt, SBN);
+        bwd_dgrad<kEpiDa><<<grid, dim3(64 * kBwdWaves), 0, s>>>(x, offsets, p.E, b, pr, c, K, N,
+                                                                 Nt, SBN);
     else
-        bwd_dgrad<kEpiPlain><<<grid, dim3(64 * dgrad_waves<kEpiPlain>()), 0, s>>>(
-            x, offsets, p.E, b, pr, c, K, N, Nt, SBN);
+        bwd_dgrad<kEpiPlain><<<grid, dim3(64 * kBwdWaves), 0, s>>>(x, offsets, p.E, b, pr, c, K,
+                                                                    N, Nt, SBN);
     return hipGetLastError();
 }
 
@@ -448,7 +447,7 @@ hipError_t launch_bwd_wgrad(const moe_problem_t& p, const void* P, const void* Q
                             const int32_t* offsets, int I, int J, float* C, hipStream_t s) {
     const int It = (I + kT - 1) / kT, Jt = (J + kT - 1) / kT;
     const int SBN = (Jt % 16 == 0) ? 16 : (Jt % 8 == 0) ? 8 : 4;
-    bwd_wgrad<<<dim3((unsigned)(p.E * It * Jt)), dim3(256), 0, s>>>(
+    bwd_wgrad<<<dim3((unsigned)(p.E * It * Jt)), dim3(64 * kBwdWaves), 0, s>>>(
         static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(Q), offsets, I, J, It, Jt,
         p.E, SBN, C);
     return hipGetLastError();
