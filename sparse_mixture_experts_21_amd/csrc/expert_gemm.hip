@@ -21,8 +21,8 @@
 // D[n][m] = W^T[n][k] . X^T[k][m] so each lane of the epilogue owns 4
 // consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
 // buffer_load ... lds (no VGPR staging) through a ring of LDS stages (2 of
-// 64-deep k-tiles for 256-row tiles, 4 of 32-deep ones for the narrower
-// layouts), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
+// 64-deep k-tiles for the 4-wave 256-row tiles, 4 of 32-deep ones for the
+// others), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
 // natural [k][n] layout in LDS and are turned into K-contiguous MFMA
 // fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
 // fragment reads for the next k-substep are interleaved with the MFMAs of
@@ -42,16 +42,18 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- bf16 MFMA
-// k-tile depth and LDS stages: the 256-row layout takes 64-deep k-tiles in 2
-// stages (one barrier per 64 k, 128 KB of LDS); the narrower layouts, which
-// stream weights, keep 32-deep k-tiles in 4 stages (prefetch 3 k-tiles ahead).
+// k-tile depth and LDS stages: the 4-wave 256-row layout takes 64-deep k-tiles
+// in 2 stages (one barrier per 64 k, 128 KB of LDS); the 8-wave layouts and
+// the narrower ones take 32-deep k-tiles in 4 stages (prefetch 3 k-tiles
+// ahead).  With two waves per SIMD to cover the barriers, the deeper prefetch
+// wins.
 template <int BM, int NW_ = 4>
 struct Cfg {
     static constexpr int NW = NW_;                    // waves: 4, or 8 (2 per SIMD)
     static constexpr int THREADS = 64 * NW;
     static constexpr int BN = 256;
-    static constexpr int BK = BM == 256 ? 64 : 32;    // k-tile depth
-    static constexpr int NS = BM == 256 ? 2 : 4;      // LDS stages
+    static constexpr int BK = (BM == 256 && NW_ == 4) ? 64 : 32;   // k-tile depth
+    static constexpr int NS = (BM == 256 && NW_ == 4) ? 2 : 4;     // LDS stages
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = NW / WM;               // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
@@ -99,7 +101,7 @@ struct TailPlan {
     int S;            // slices per tail tile (1: no cut)
 };
 
-template <int BM>
+template <int BM, int NW = 4>
 __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int Nt,
                                               int ncu, int nk, bool allow) {
     TailPlan pl;
@@ -108,7 +110,7 @@ __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offset
     const int R = mtiles * Nt;
     pl.tail = R % ncu;
     int S = pl.tail > 0 ? min(ncu, kMaxUnits) / pl.tail : 1;
-    S = min(S, nk / Cfg<BM>::NS);
+    S = min(S, nk / Cfg<BM, NW>::NS);
     if (!allow || S < 2) {
         pl.S = 1;
         pl.tail = 0;
@@ -573,7 +575,7 @@ __global__ __launch_bounds__((64 * gemm_waves<BM, ACT>())) void ffn_gemm_bf16(
     // re-reads weight tiles across row tiles and keeps the default policy.
     constexpr bool kNtW = BM <= 128;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, part != nullptr);
+    const TailPlan pl = tail_plan<BM, NW>(offsets, E, Nt, ncu, nk, part != nullptr);
     const int p = blockIdx.x;
     int tile = p, kb = 0, nkr = nk, unit = -1;
     if (p >= pl.full) {
@@ -631,9 +633,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre, int K, int N, int Nt, int SBN, int ncu,
     const float* __restrict__ part) {
-    using G = Cfg<BM>;
+    using G = Cfg<BM, gemm_waves<BM, ACT>()>;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, true);
+    const TailPlan pl = tail_plan<BM, gemm_waves<BM, ACT>()>(offsets, E, Nt, ncu, nk, true);
     const int i = blockIdx.x / FixCfg<BM>::CHUNKS, c = blockIdx.x % FixCfg<BM>::CHUNKS;
     if (pl.S < 2 || i >= pl.tail) return;
     int mt, nt;
