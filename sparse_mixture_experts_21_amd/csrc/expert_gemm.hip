@@ -15,14 +15,13 @@
 // synchronisation is needed; surplus workgroups return at once and experts
 // with no rows cost nothing (their weights are never read).
 //
-// bf16 kernel (gfx950): 256 threads (512 for the 256-row tile of the GEMM
-// with an activation: 2 waves per SIMD), tile BN = 256 output columns x BM rows,
+// bf16 kernel (gfx950): 256 threads, tile BN = 256 output columns x BM rows,
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, issued as
 // D[n][m] = W^T[n][k] . X^T[k][m] so each lane of the epilogue owns 4
 // consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
 // buffer_load ... lds (no VGPR staging) through a ring of LDS stages (2 of
-// 64-deep k-tiles for the 4-wave 256-row tiles, 4 of 32-deep ones for the
-// others), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
+// 64-deep k-tiles for 256-row tiles, 4 of 32-deep ones for the narrower
+// layouts), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
 // natural [k][n] layout in LDS and are turned into K-contiguous MFMA
 // fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
 // fragment reads for the next k-substep are interleaved with the MFMAs of
@@ -42,20 +41,16 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- bf16 MFMA
-// k-tile depth and LDS stages: the 4-wave 256-row layout takes 64-deep k-tiles
-// in 2 stages (one barrier per 64 k, 128 KB of LDS); the 8-wave layouts and
-// the narrower ones take 32-deep k-tiles in 4 stages (prefetch 3 k-tiles
-// ahead).  With two waves per SIMD to cover the barriers, the deeper prefetch
-// wins.
-template <int BM, int NW_ = 4>
+// k-tile depth and LDS stages: the 256-row layout takes 64-deep k-tiles in 2
+// stages (one barrier per 64 k, 128 KB of LDS); the narrower layouts, which
+// stream weights, keep 32-deep k-tiles in 4 stages (prefetch 3 k-tiles ahead).
+template <int BM>
 struct Cfg {
-    static constexpr int NW = NW_;                    // waves: 4, or 8 (2 per SIMD)
-    static constexpr int THREADS = 64 * NW;
     static constexpr int BN = 256;
-    static constexpr int BK = (BM == 256 && NW_ == 4) ? 64 : 32;   // k-tile depth
-    static constexpr int NS = (BM == 256 && NW_ == 4) ? 2 : 4;     // LDS stages
+    static constexpr int BK = BM == 256 ? 64 : 32;    // k-tile depth
+    static constexpr int NS = BM == 256 ? 2 : 4;      // LDS stages
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
-    static constexpr int WN = NW / WM;               // waves along n
+    static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
     static constexpr int FN = TN / 32, FM = TM / 32; // 32x32 MFMA tiles per wave
     static constexpr int W_BYTES = BK * BN * 2;      // weight tile [BK][BN], 512-byte rows
@@ -64,10 +59,8 @@ struct Cfg {
     static constexpr int RPB = 64 / CPR;             // X rows per 1 KB DMA block
     static constexpr int RSH = (CPR == 4) ? 2 : 1;   // X swizzle: chunk ^= (m >> RSH) % CPR
     static constexpr int STAGE = W_BYTES + X_BYTES;
-    static constexpr int WI = W_BYTES / (1024 * NW); // 1 KB DMA blocks per wave (weights)
-    static constexpr int XI = X_BYTES / (1024 * NW); // 1 KB DMA blocks per wave (rows)
-    static_assert(WI * 1024 * NW == W_BYTES && XI * 1024 * NW == X_BYTES && XI >= 1,
-                  "the stage tiles split into 1 KB blocks over the waves");
+    static constexpr int WI = W_BYTES / 4096;        // 1 KB DMA blocks per wave (weights)
+    static constexpr int XI = X_BYTES / 4096;        // 1 KB DMA blocks per wave (rows)
     static_assert(BK == 32 || BK == 64, "k-tile depth");
     static_assert(NS >= 2, "stages");
     static constexpr int OP = BN * 2 + 16;           // output staging row pitch (bytes)
@@ -75,10 +68,6 @@ struct Cfg {
     static constexpr int LDS_BYTES = (NS * STAGE > BM * OP) ? NS * STAGE : BM * OP;
     static constexpr int UNIT = BM * BN;             // floats of one fp32 partial tile
 };
-
-// A wave's accumulators: FN x FM 32x32 MFMA tiles.
-template <int BM, int NW>
-using AccTile = f32x16_t[Cfg<BM, NW>::FN][Cfg<BM, NW>::FM];
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
@@ -101,7 +90,7 @@ struct TailPlan {
     int S;            // slices per tail tile (1: no cut)
 };
 
-template <int BM, int NW = 4>
+template <int BM>
 __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int Nt,
                                               int ncu, int nk, bool allow) {
     TailPlan pl;
@@ -110,7 +99,7 @@ __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offset
     const int R = mtiles * Nt;
     pl.tail = R % ncu;
     int S = pl.tail > 0 ? min(ncu, kMaxUnits) / pl.tail : 1;
-    S = min(S, nk / Cfg<BM, NW>::NS);
+    S = min(S, nk / Cfg<BM>::NS);
     if (!allow || S < 2) {
         pl.S = 1;
         pl.tail = 0;
@@ -139,12 +128,12 @@ struct TileRef {
 // DMA pipeline and MFMA loop over the k-tiles [kb, kb + nkr) of tile `tr`,
 // accumulating into acc (the caller zeroes it).  `lds` holds Cfg<BM>::LDS_BYTES.
 // NTW: weight loads carry the nontemporal hint (see ffn_gemm_bf16).
-template <int BM, int NW, bool NTW>
+template <int BM, bool NTW>
 __device__ __forceinline__ void gemm_mainloop(
     const TileRef& tr, int kb, int nkr, char* lds, const uint16_t* __restrict__ X,
     uint32_t x_bytes, const int32_t* __restrict__ rowmap, const uint16_t* __restrict__ W, int K,
-    int N, AccTile<BM, NW>& acc) {
-    using G = Cfg<BM, NW>;
+    int N, f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM]) {
+    using G = Cfg<BM>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -162,7 +151,7 @@ __device__ __forceinline__ void gemm_mainloop(
     uint32_t woff[G::WI];
 #pragma unroll
     for (int q = 0; q < G::WI; ++q) {
-        const int blk = NW * q + wave;                      // 1 KB block = 2 weight rows
+        const int blk = 4 * q + wave;                       // 1 KB block = 2 weight rows
         const int k = 2 * blk + (lane >> 5);
         const int c = (lane & 31) ^ (4 * (k & 3));           // logical 16-byte chunk
         woff[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)(tr.n0 + 8 * c) * 2u;
@@ -171,7 +160,7 @@ __device__ __forceinline__ void gemm_mainloop(
     int xk[G::XI];
 #pragma unroll
     for (int q = 0; q < G::XI; ++q) {
-        const int blk = NW * q + wave;                      // 1 KB block = RPB rows
+        const int blk = 4 * q + wave;                       // 1 KB block = RPB rows
         const int row = G::RPB * blk + lane / G::CPR;
         const int c = (lane % G::CPR) ^ ((row >> G::RSH) % G::CPR);
         const int rr = min(row, tile_rows - 1);             // row within the tile
@@ -189,14 +178,14 @@ __device__ __forceinline__ void gemm_mainloop(
         const int k0 = (kb + t) * G::BK;
         if (q < G::WI) {
             const uint32_t o = woff[q] + (uint32_t)(kb + t) * wstep;
-            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((NW * q + wave) * 1024));
+            const uint32_t l = __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * q + wave) * 1024));
             if constexpr (NTW) dma16_nt(w_rsrc, o, l);
             else dma16(w_rsrc, o, l);
         } else {
             const int qx = q - G::WI;
             const uint32_t o = (k0 + xk[qx] < K) ? xoff[qx] + (uint32_t)k0 * 2u : kOob;
             dma16(x_rsrc, o,
-                  __builtin_amdgcn_readfirstlane(st + (uint32_t)(G::W_BYTES + (NW * qx + wave) * 1024)));
+                  __builtin_amdgcn_readfirstlane(st + (uint32_t)(G::W_BYTES + (4 * qx + wave) * 1024)));
         }
     };
 
@@ -361,7 +350,7 @@ __device__ __forceinline__ void store_staged(const TileRef& tr, const char* lds,
     const int rows = min(G::BM_ROWS, tr.n_rows - tr.m0);
     const int chunks = min(G::BN, N - tr.n0) / 8;         // 16-byte chunks per row (N % 8 == 0)
     uint16_t* cbase = out + (int64_t)(tr.row_begin + tr.m0) * N + tr.n0;
-    for (int idx = threadIdx.x; idx < G::BM_ROWS * (G::BN / 8); idx += (int)blockDim.x) {
+    for (int idx = threadIdx.x; idx < G::BM_ROWS * (G::BN / 8); idx += 256) {
         const int r = idx / (G::BN / 8), c = idx % (G::BN / 8);
         if (r < rows && c < chunks)
             *reinterpret_cast<u32x4_t*>(cbase + (int64_t)r * N + c * 8) =
@@ -381,13 +370,13 @@ __device__ __forceinline__ void store_staged(const TileRef& tr, const char* lds,
 // by it.  Then the tile goes out in two halves of its rows (each wave's
 // accumulator rows j < FM/2, then the rest), h and act' staged side by side in
 // the same LDS, so both are written as full rows.
-template <int BM, int NW, int ACT, bool SAVE>
+template <int BM, int ACT, bool SAVE>
 __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
-                                              AccTile<BM, NW>& acc,
+                                              f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
                                               char* lds, const uint16_t* __restrict__ bias,
                                               uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
                                               int N) {
-    using G = Cfg<BM, NW>;
+    using G = Cfg<BM>;
     wait_lgkm0();
     lds_barrier();
     const uint16_t* be = bias ? bias + (int64_t)tr.e * N : nullptr;
@@ -469,7 +458,7 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
                 }
             }
             lds_barrier();
-            for (int idx = threadIdx.x; idx < HROWS * (G::BN / 8); idx += (int)blockDim.x) {
+            for (int idx = threadIdx.x; idx < HROWS * (G::BN / 8); idx += 256) {
                 const int lr = idx / (G::BN / 8), c = idx % (G::BN / 8);
                 const int r = (lr / HR) * G::TM + hh * HR + lr % HR;  // row of the tile
                 if (r < rows && c < chunks) {
@@ -488,10 +477,10 @@ __device__ __forceinline__ void gemm_epilogue(const TileRef& tr,
 // per slice); only the tile's real rows are written (and later read), so a
 // slice of a tile with a few rows costs a few KB.  A lane holds columns
 // 8 g + 4 half + 0..3 of row l32 of each 32x32 MFMA tile (acc[i][j][4 g + q]).
-template <int BM, int NW>
-__device__ __forceinline__ void store_partial(const AccTile<BM, NW>& acc,
+template <int BM>
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM],
                                               float* __restrict__ dst, int rows) {
-    using G = Cfg<BM, NW>;
+    using G = Cfg<BM>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
     const int l32 = lane & 31, half = lane >> 5;
@@ -511,12 +500,12 @@ __device__ __forceinline__ void store_partial(const AccTile<BM, NW>& acc,
     }
 }
 
-template <int BM, int NW>
-__device__ __forceinline__ void zero_acc(AccTile<BM, NW>& acc) {
+template <int BM>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM]) {
 #pragma unroll
-    for (int i = 0; i < Cfg<BM, NW>::FN; ++i)
+    for (int i = 0; i < Cfg<BM>::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg<BM, NW>::FM; ++j)
+        for (int j = 0; j < Cfg<BM>::FM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
@@ -528,8 +517,8 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
     return find_tile<BM>(offsets, E, mt, tr.e, tr.m0, tr.row_begin, tr.n_rows);
 }
 
-// One whole tile with the row layout of Cfg<TB, NW> (TB <= the kernel's BM).
-template <int TB, int NW, int ACT, bool NTW, bool SAVE>
+// One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
+template <int TB, int ACT, bool NTW, bool SAVE>
 __device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
                                            const uint16_t* __restrict__ X, uint32_t x_bytes,
                                            const int32_t* __restrict__ rowmap,
@@ -538,34 +527,25 @@ __device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
                                            uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
                                            int K, int N) {
     // k-tiles of this layout's own depth (the layouts differ in k-tile depth)
-    const int nk = (K + Cfg<TB, NW>::BK - 1) / Cfg<TB, NW>::BK;
-    f32x16_t acc[Cfg<TB, NW>::FN][Cfg<TB, NW>::FM];
-    zero_acc<TB, NW>(acc);
-    gemm_mainloop<TB, NW, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
-    gemm_epilogue<TB, NW, ACT, SAVE>(tr, acc, lds, bias, C, Cpre, N);
+    const int nk = (K + Cfg<TB>::BK - 1) / Cfg<TB>::BK;
+    f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
+    zero_acc<TB>(acc);
+    gemm_mainloop<TB, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_epilogue<TB, ACT, SAVE>(tr, acc, lds, bias, C, Cpre, N);
 }
-
-// Waves per workgroup: the 256-row tile of the GEMM with an activation runs 8
-// waves (2 per SIMD, each a 128 x 64 block of the tile), so one wave's MFMAs
-// cover the other's LDS reads and its long epilogue; the GEMM without one
-// keeps 4 (measured: the second wave gains nothing there).
-template <int BM, int ACT>
-constexpr int gemm_waves() { return (BM == 256 && ACT != kActNone) ? 8 : 4; }
 
 // Workgroup p: whole tile p (p < full), or one K slice of a tail tile.  `part`
 // (nullable) is the fp32 slice buffer; without it no tile is cut.  The last
 // row tile of an expert is usually short: with at most 128 (64) real rows it
-// runs the 128-row (64-row) layout, whose waves split the columns instead of
-// idling on rows that do not exist (the 8-wave kernel has no 64-row layout:
-// its 4 KB row stage does not split over 8 waves).
+// runs the 128-row (64-row) layout, whose four waves split the columns instead
+// of idling on rows that do not exist.
 template <int BM, int ACT, bool SAVE>
-__global__ __launch_bounds__((64 * gemm_waves<BM, ACT>())) void ffn_gemm_bf16(
+__global__ __launch_bounds__(256) void ffn_gemm_bf16(
     const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
     int K, int N, int Nt, int SBN, int ncu, float* __restrict__ part) {
-    constexpr int NW = gemm_waves<BM, ACT>();
-    using G = Cfg<BM, NW>;
+    using G = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
     static_assert(BM < 128 || Cfg<64>::LDS_BYTES <= G::LDS_BYTES, "64-row layout fits");
     static_assert(BM < 256 || Cfg<128>::LDS_BYTES <= G::LDS_BYTES, "128-row layout fits");
@@ -575,7 +555,7 @@ __global__ __launch_bounds__((64 * gemm_waves<BM, ACT>())) void ffn_gemm_bf16(
     // re-reads weight tiles across row tiles and keeps the default policy.
     constexpr bool kNtW = BM <= 128;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM, NW>(offsets, E, Nt, ncu, nk, part != nullptr);
+    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, part != nullptr);
     const int p = blockIdx.x;
     int tile = p, kb = 0, nkr = nk, unit = -1;
     if (p >= pl.full) {
@@ -593,27 +573,27 @@ __global__ __launch_bounds__((64 * gemm_waves<BM, ACT>())) void ffn_gemm_bf16(
     if (!tile_ref<BM>(offsets, E, mt, nt, tr)) return;
     if (unit < 0) {
         const int rows = tr.n_rows - tr.m0;
-        if constexpr (BM >= 128 && NW == 4) {
+        if constexpr (BM >= 128) {
             if (rows <= 64) {
-                whole_tile<64, NW, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre,
-                                                    K, N);
+                whole_tile<64, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                                                  N);
                 return;
             }
         }
         if constexpr (BM >= 256) {
             if (rows <= 128) {
-                whole_tile<128, NW, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C,
-                                                     Cpre, K, N);
+                whole_tile<128, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                                                   N);
                 return;
             }
         }
-        whole_tile<BM, NW, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
+        whole_tile<BM, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
         return;
     }
     f32x16_t acc[G::FN][G::FM];
-    zero_acc<BM, NW>(acc);
-    gemm_mainloop<BM, NW, kNtW>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
-    store_partial<BM, NW>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
+    zero_acc<BM>(acc);
+    gemm_mainloop<BM, kNtW>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
+    store_partial<BM>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
 }
 
 // Tail tiles: workgroup (tile i, chunk c) takes rows 16 c .. 16 c + 15 of the
@@ -633,9 +613,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre, int K, int N, int Nt, int SBN, int ncu,
     const float* __restrict__ part) {
-    using G = Cfg<BM, gemm_waves<BM, ACT>()>;
+    using G = Cfg<BM>;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM, gemm_waves<BM, ACT>()>(offsets, E, Nt, ncu, nk, true);
+    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, true);
     const int i = blockIdx.x / FixCfg<BM>::CHUNKS, c = blockIdx.x % FixCfg<BM>::CHUNKS;
     if (pl.S < 2 || i >= pl.tail) return;
     int mt, nt;
@@ -797,8 +777,7 @@ hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, co
                  int N, int Mt, int Nt, int SBN, int ncu, float* part, hipEvent_t mid,
                  hipStream_t s) {
     const int units = std::min(ncu, kMaxUnits);
-    const dim3 block(64 * gemm_waves<BM, ACT>());
-    const dim3 grid((unsigned)((int64_t)Mt * Nt + units));
+    const dim3 block(256), grid((unsigned)((int64_t)Mt * Nt + units));
     if (cpre)
         ffn_gemm_bf16<BM, ACT, true><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b, c,
                                                             cpre, K, N, Nt, SBN, ncu, part);
@@ -809,8 +788,7 @@ hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, co
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
     if (part)
-        ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), dim3(256), 0,
-                                  s>>>(
+        ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
             offsets, E, b, c, cpre, K, N, Nt, SBN, ncu, part);
     return hipGetLastError();
 }
