@@ -9,9 +9,9 @@
 //   wgrad   C[e][i][j] = sum_r P[r][i] Q[r][j]       both operands row-major over r
 //           (dW2[e] = h^T dy:  P = h, Q = dy;  dW1[e] = xp^T da:  P = xp, Q = da)
 //
-// The tile machinery is the forward's: 256 x 256 output tiles, 8 waves (2 per
-// SIMD) of 128 rows x 64 columns on v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation, operands moved
+// The tile machinery is the forward's (256 x 256 output tiles on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation), but with 8 waves (2 per
+// SIMD) of 128 rows x 64 columns where the forward runs 4; operands moved
 // HBM -> LDS by buffer_load ... lds through a 128 KB ring (dgrad: 2 stages of
 // 64-deep k-tiles; wgrad: 4 stages of 32-deep ones).  An
 // operand is either K-contiguous ("row" layout: LDS [idx][k], 64-byte rows,
