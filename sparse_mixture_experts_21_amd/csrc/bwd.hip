@@ -109,54 +109,75 @@ __global__ __launch_bounds__(kBT) void bwd_token(
     if (e < E) dl[t * E + e] = p * (dp - pdp) + g_z * 2.0f * lse * p / (float)T;
 }
 
-// One workgroup per token: dx[t] = sum over kept slots (slot order) of dxe
-// rows + sum_e dl[t][e] Wg[h][e] (Wg [H][E] bf16), fp32, rounded once.
+// dx[t] = sum over kept slots (slot order) of dxe rows + sum_e dl[t][e]
+// Wg[h][e] (Wg [H][E] bf16), fp32, rounded once.  kDxTok tokens per
+// workgroup, so the gate rows a thread needs are loaded once for all of them:
+// into registers when E % 8 == 0 and E <= 16 (REG), else re-read per token
+// (they stay in the cache).  Per token and 8 hidden
+// units h = 8 v .. 8 v + 7: the kept slots' dxe rows in slot order, plus the
+// gate term sum_e dl[t][e] Wg[h][e] in e order.
+constexpr int kDxTok = 16;
+
+template <bool REG>
 __global__ __launch_bounds__(kBT) void bwd_dx(const u32x4_t* __restrict__ dxe,
                                               const int32_t* __restrict__ pos,
                                               const float* __restrict__ dl,
                                               const uint16_t* __restrict__ Wg, int E, int k,
-                                              int64_t vec, u32x4_t* __restrict__ dx) {
-    __shared__ float s_dl[kMaxE];
-    const int64_t t = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += kBT) s_dl[e] = dl[t * E + e];
+                                              int64_t vec, int64_t T, u32x4_t* __restrict__ dx) {
+    __shared__ float s_dl[kDxTok][kMaxE];
+    const int64_t t0 = (int64_t)blockIdx.x * kDxTok;
+    const int nt = (int)min((int64_t)kDxTok, T - t0);
+    for (int i = threadIdx.x; i < nt * E; i += kBT) s_dl[i / E][i % E] = dl[t0 * E + i];
     __syncthreads();
     for (int64_t v = threadIdx.x; v < vec; v += kBT) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < k; ++s) {
-            const int32_t r = pos[t * k + s];
-            if (r < 0) continue;
-            const u32x4_t d = dxe[(int64_t)r * vec + v];
+        // REG: the 8 gate rows of this vector's hidden units (8 E contiguous bf16)
+        u32x4_t wreg[8][2];
+        if constexpr (REG) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] += bf16_lo(d[q]);
-                acc[2 * q + 1] += bf16_hi(d[q]);
-            }
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    if (8 * c < E)
+                        wreg[u][c] = *reinterpret_cast<const u32x4_t*>(Wg + (8 * v + u) * E + 8 * c);
         }
-        // gate term: the 8 hidden units h = 8 v .. 8 v + 7, whose gate rows are
-        // 8 E contiguous elements of Wg: 16-byte loads when E % 8 == 0
+        for (int j = 0; j < nt; ++j) {
+            const int64_t t = t0 + j;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < k; ++s) {
+                const int32_t r = pos[t * k + s];
+                if (r < 0) continue;
+                const u32x4_t d = dxe[(int64_t)r * vec + v];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint16_t* wr = Wg + (8 * v + u) * E;
-            float g = 0.f;
-            if ((E & 7) == 0) {
-                for (int e0 = 0; e0 < E; e0 += 8) {
-                    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wr + e0);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        g = fmaf(s_dl[e0 + 2 * q], bf16_lo(wv[q]), g);
-                        g = fmaf(s_dl[e0 + 2 * q + 1], bf16_hi(wv[q]), g);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += bf16_lo(d[q]);
+                    acc[2 * q + 1] += bf16_hi(d[q]);
                 }
-            } else {
-                for (int e = 0; e < E; ++e)
-                    g = fmaf(s_dl[e], __uint_as_float((uint32_t)wr[e] << 16), g);
             }
-            acc[u] += g;
-        }
-        u32x4_t o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-        dx[t * vec + v] = o;
+            for (int u = 0; u < 8; ++u) {
+                float g = 0.f;
+                if constexpr (REG) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        if (8 * c >= E) break;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            g = fmaf(s_dl[j][8 * c + 2 * q], bf16_lo(wreg[u][c][q]), g);
+                            g = fmaf(s_dl[j][8 * c + 2 * q + 1], bf16_hi(wreg[u][c][q]), g);
+                        }
+                    }
+                } else {
+                    const uint16_t* wr = Wg + (8 * v + u) * E;
+                    for (int e = 0; e < E; ++e)
+                        g = fmaf(s_dl[j][e], __uint_as_float((uint32_t)wr[e] << 16), g);
+                }
+                acc[u] += g;
+            }
+            u32x4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+            dx[t * vec + v] = o;
+        }
     }
 }
 
@@ -285,9 +306,14 @@ hipError_t launch_bwd_token(const moe_problem_t& p, const void* dout, const void
 hipError_t launch_bwd_dx(const moe_problem_t& p, const void* dxe, const int32_t* pos,
                          const float* dl, const void* Wg, void* dx, hipStream_t s) {
     const int64_t vec = (int64_t)p.H * 2 / 16;
-    bwd_dx<<<dim3((unsigned)p.T), dim3(kBT), 0, s>>>(
-        static_cast<const u32x4_t*>(dxe), pos, dl, static_cast<const uint16_t*>(Wg), p.E, p.k, vec,
-        static_cast<u32x4_t*>(dx));
+    const dim3 grid((unsigned)((p.T + kDxTok - 1) / kDxTok));
+    auto* d = static_cast<const u32x4_t*>(dxe);
+    auto* w = static_cast<const uint16_t*>(Wg);
+    auto* o = static_cast<u32x4_t*>(dx);
+    if (p.E % 8 == 0 && p.E <= 16)
+        bwd_dx<true><<<grid, dim3(kBT), 0, s>>>(d, pos, dl, w, p.E, p.k, vec, p.T, o);
+    else
+        bwd_dx<false><<<grid, dim3(kBT), 0, s>>>(d, pos, dl, w, p.E, p.k, vec, p.T, o);
     return hipGetLastError();
 }
 
