@@ -58,6 +58,8 @@ def lib():
         L.orc_backward_tokens.argtypes = [P] + [vp] * 8 + [vp, ctypes.c_double, ctypes.c_double,
                                                           vp, ctypes.c_int64, vp]
         L.orc_backward_weight_entries.argtypes = [P] + [vp] * 8 + [vp, vp, ctypes.c_int64, vp]
+        L.orc_backward_gate.argtypes = [P] + [vp] * 8 + [vp, ctypes.c_double, ctypes.c_double,
+                                                          vp, vp]
         L.orc_num_threads.argtypes = []
         _lib = L
     return _lib
@@ -282,6 +284,17 @@ def backward_tokens(spec, inp, dout, tokens: Sequence[int], g_aux: float = 0.0, 
                                      float(g_z), _ptr(tok), tok.shape[0], _ptr(dx)),
            "backward_tokens")
     return dx
+
+
+def backward_gate(spec, inp, dout, g_aux: float = 0.0, g_z: float = 0.0,
+                  given_logits: Optional[np.ndarray] = None):
+    """(dWg [H][E], dbg [E]) of the same objective as backward(), computed
+    without the expert-weight and dx terms (one forward's work)."""
+    dWg = np.empty((spec.H, spec.E))
+    dbg = np.empty(spec.E)
+    _check(lib().orc_backward_gate(*_bwd_common(spec, inp, dout, given_logits), float(g_aux),
+                                   float(g_z), _ptr(dWg), _ptr(dbg)), "backward_gate")
+    return dWg, dbg
 
 
 def backward_weight_entries(spec, inp, dout, entries, given_logits=None) -> np.ndarray:

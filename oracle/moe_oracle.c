@@ -690,6 +690,72 @@ int orc_backward_tokens(const orc_problem* p, const void* x, const void* Wg, con
     return bad ? -3 : 0;
 }
 
+/* The gate gradients dWg and dbg alone, by the definition orc_backward uses
+ * and in its order: every token's kept rows run forward for dw_s = dout . y,
+ * token_dl gives dl, then dbg[e] = sum_t dl[t][e] and dWg[i][e] =
+ * sum_t x[t][i] dl[t][e] over ascending t.  No expert-weight or dx term is
+ * formed, so it needs one forward's work and memory for dl only. */
+int orc_backward_gate(const orc_problem* p, const void* x, const void* Wg, const void* bg,
+                      const void* W1, const void* b1, const void* W2, const void* b2,
+                      const double* logits_in, const void* dout, double g_aux, double g_z,
+                      double* dWg, double* dbg) {
+    if (!valid(p) || !x || !Wg || !W1 || !W2 || !dout) return -1;
+    const int64_t T = p->T;
+    const int H = p->H, E = p->E, k = p->k, F = p->F, dt = p->dtype;
+    bwd_route r;
+    int rc = bwd_route_make(p, x, Wg, bg, logits_in, &r);
+    if (rc) return rc;
+    double* DL = (double*)calloc((size_t)(T * E), sizeof(double));
+    if (!DL) {
+        bwd_route_free(&r);
+        return -2;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* a = (double*)malloc(sizeof(double) * (size_t)F);
+        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dw = (double*)malloc(sizeof(double) * (size_t)k);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)E);
+        if (!xr || !a || !y || !dw || !dp) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < T; ++t) {
+            if (!xr || !a || !y || !dw || !dp) continue;
+            for (int i = 0; i < H; ++i) xr[i] = load(x, t * H + i, dt);
+            for (int s = 0; s < k; ++s) {
+                dw[s] = 0.0;
+                if (r.pos[t * k + s] < 0) continue;
+                row_forward(p, xr, r.idx[t * k + s], W1, b1, W2, b2, a, y);
+                for (int o = 0; o < H; ++o) dw[s] += load(dout, t * H + o, dt) * y[o];
+            }
+            token_dl(p, &r, t, dw, g_aux, g_z, dp, DL + t * E);
+        }
+        free(xr); free(a); free(y); free(dw); free(dp);
+    }
+    if (!bad) {
+        for (int e = 0; e < E; ++e) {
+            if (dbg) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t) acc += DL[t * E + e];
+                dbg[e] = acc;
+            }
+            if (dWg)
+                for (int i = 0; i < H; ++i) {
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < T; ++t) acc += load(x, t * H + i, dt) * DL[t * E + e];
+                    dWg[(int64_t)i * E + e] = acc;
+                }
+        }
+    }
+    free(DL);
+    bwd_route_free(&r);
+    return bad ? -2 : 0;
+}
+
 int orc_backward_weight_entries(const orc_problem* p, const void* x, const void* Wg,
                                 const void* bg, const void* W1, const void* b1, const void* W2,
                                 const void* b2, const double* logits_in, const void* dout,

@@ -116,6 +116,14 @@ int orc_backward_tokens(const orc_problem* p, const void* x, const void* Wg, con
                         const double* logits_in, const void* dout, double g_aux, double g_z,
                         const int64_t* tokens, int64_t ntok, double* dx);
 
+/* The gate gradients dWg [H][E] and dbg [E] alone (either may be NULL): the
+ * same definition and summation order as orc_backward, with one forward's
+ * work (every kept row's y for dw) and none of the expert-weight terms. */
+int orc_backward_gate(const orc_problem* p, const void* x, const void* Wg, const void* bg,
+                      const void* W1, const void* b1, const void* W2, const void* b2,
+                      const double* logits_in, const void* dout, double g_aux, double g_z,
+                      double* dWg, double* dbg);
+
 /* Single entries of the expert-weight gradients: entries [n][4] = (kind, e,
  * i, j) with kind 1: dW1[e][i][j], 2: dW2[e][i][j], 3: db1[e][j], 4: db2[e][j];
  * each is summed over the expert's kept rows in token order. */

@@ -28,19 +28,37 @@ constexpr uint32_t kOob = 0x80000000u;   // an offset beyond every resource's ra
 
 // 16 bytes per lane from global memory straight into LDS (M0 + 16 * lane);
 // no VGPR is written, so nothing is left in flight in registers.  Completion
-// is tracked with vmcnt by the caller; the compiler does not count these.
+// is tracked with vmcnt by the caller; the compiler does not count these (the
+// compiler's own LDS-DMA builtin makes it wait for every DMA in flight before
+// the next LDS read, which would drain the prefetch ring).
+// M0 is reserved to the compiler, so the helper saves it, loads the LDS
+// address, waits the one wait state gfx9 needs between an M0 write and an
+// LDS DMA that reads it (s_nop 0), issues the DMA (which takes M0 at issue)
+// and restores M0: whatever the compiler keeps in M0 survives the call.
+#define MOE_DMA16(HINT)                                                           \
+    do {                                                                         \
+        uint32_t saved_m0;                                                       \
+        asm volatile("s_mov_b32 %0, m0\n\t"                                       \
+                     "s_mov_b32 m0, %3\n\t"                                       \
+                     "s_nop 0\n\t"                                                \
+                     "buffer_load_dwordx4 %1, %2, 0 offen " HINT "lds\n\t"         \
+                     "s_mov_b32 m0, %0"                                           \
+                     : "=&s"(saved_m0)                                            \
+                     : "v"(voff), "s"(r), "s"(lds)                                \
+                     : "memory");                                                 \
+    } while (0)
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory");
+    MOE_DMA16("");
 }
 
 // As dma16, with the nontemporal hint: the lines are not kept in the
 // last-level cache, so streaming a large input once neither evicts nor
 // writes back other kernels' lines on the way.
 __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory");
+    MOE_DMA16("nt ");
 }
+#undef MOE_DMA16
 
 // s_waitcnt vmcnt(n) (gfx9 encoding; lgkmcnt and expcnt left unconstrained).
 template <int N>

@@ -7,6 +7,10 @@ Tolerances (floating-point outputs against the fp64 oracle):
   rms over the same row (token or expert row) of the reference: a floor that
   avoids dividing by values near 0 without letting rows that capacity dropped
   (exact zeros) dilute it.
+* and, over the whole compared tensor, ||gpu - ref||_2 / ||ref||_2 <= 5e-3
+  (bf16) or 1e-5 (fp32): three bf16 roundings (h, y, out), each with a
+  relative rms error of about 1.6e-3 and independent per element, give
+  about 2.8e-3 at most.
 * logits: |d| <= 1e-5 (fp32) / 1e-4 (bf16 inputs, fp32 dot over H);
   topk_w: |d| <= 1e-5;  aux, z: 1e-5 relative.
 Integer outputs (indices, counts, offsets, positions) must match exactly, and
@@ -24,6 +28,7 @@ import sparse_mixture_experts_21_amd as moe
 import workloads as W
 
 DEV = "cuda"
+REL_L2_LIMIT = {"bf16": 5e-3, "f32": 1e-5}
 
 
 def say(*a):
@@ -137,6 +142,11 @@ def assert_close_storage(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str
     nrm = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(gpu - ref)) / nrm if nrm > 0 else float(np.linalg.norm(gpu))
     say(f"    {what}: max abs {float(err.max()):.3e}, rel l2 {rel:.3e}")
+    # A bias shared by many elements (a lost or doubled term, a scale off by
+    # 1%) can stay inside the elementwise bound; the relative L2 error of the
+    # whole tensor cannot hide it.
+    lim = REL_L2_LIMIT[dtype]
+    assert rel <= lim, f"{what}: relative L2 error {rel:.3e} > {lim:g}"
 
 
 def logits_tol(spec) -> float:

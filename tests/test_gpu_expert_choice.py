@@ -7,6 +7,8 @@ match bit for bit, probs within 1e-5.  The logits themselves are compared with
 the oracle's fp64 logits, and the layer output with the oracle's expert-choice
 layer (on the same selection) within the storage-type tolerance.
 """
+import time
+
 import numpy as np
 import pytest
 
@@ -141,7 +143,10 @@ def test_ec_route_equals_forward_bitwise(spec):
     assert r1["offsets"].cpu().tolist() == [e * (spec.T // g) * C for e in range(spec.E + 1)]
 
 
-def test_ec_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_ec_full_size():
+    """The 16384-token Mixtral-shaped expert-choice layer (2048-token groups):
+    the selection exactly, and the output of every token against the oracle."""
     spec = W.CONFIGS["c5e"]
     g = spec.ec_group
     say(f"[expert choice full size] {spec.name}")
@@ -160,12 +165,11 @@ def test_ec_full_size_sampled():
     taken = (r["rowof"] >= 0).sum(axis=1)
     say(f"    C {r['C']}, rows {spec.E * (spec.T // g) * r['C']}, tokens taken by 0 experts "
         f"{int((taken == 0).sum())}, by >= 3 experts {int((taken >= 3).sum())}")
-    rng = np.random.default_rng(0)
-    toks = np.unique(np.concatenate([np.arange(8), np.arange(spec.T - 8, spec.T),
-                                     rng.choice(spec.T, 40, replace=False),
-                                     np.nonzero(taken == 0)[0][:4],
-                                     np.nonzero(taken == taken.max())[0][:4]]))
+    got = as_f64(o["out"])
+    del o, d, ws
+    t0 = time.perf_counter()
     ref = om.ec_forward_tokens(spec, inp["x"], r["rowof"], r["probs"], inp["W1"], inp.get("b1"),
-                               inp["W2"], inp.get("b2"), toks)
-    got = as_f64(o["out"][torch.from_numpy(toks).to(DEV)])
-    assert_close_storage(got, ref, spec.dtype, f"out[{len(toks)} sampled tokens]")
+                               inp["W2"], inp.get("b2"), np.arange(spec.T))
+    say(f"    oracle over all {spec.T} tokens: {time.perf_counter() - t0:.1f} s")
+    assert_close_storage(got, ref, spec.dtype, f"out[all {spec.T} tokens]")
+    assert np.all(got[taken == 0] == 0.0)

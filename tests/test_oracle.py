@@ -504,3 +504,23 @@ def test_backward_tokens_and_weight_entries_match_full(oracle_mod):
     ref = [g["dW1"][0, 3, 7], g["dW1"][4, 15, 39], g["dW2"][2, 11, 5], g["dW2"][3, 0, 15],
            g["db1"][1, 20], g["db2"][4, 9]]
     np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("case", [dict(T=30, E=5, k=2, cf=0.75, dtype="bf16"),
+                                  dict(T=24, E=4, k=1, cf=0.0, act="silu"),
+                                  dict(T=40, E=8, k=3, cf=0.5, dtype="bf16", biases=False)],
+                         ids=["bf16_drops", "silu_k1", "k3_heavy_drops"])
+def test_backward_gate_matches_full(oracle_mod, case):
+    """The gate-only gradients (used where the full backward is too large)
+    equal the full backward's dWg and dbg bit for bit: the same terms in the
+    same order, on the oracle's own and on given logits."""
+    spec = tiny(**case)
+    inp = W.generate(spec, workers=1)
+    dout = W.synthetic_rows(spec, spec.T, tid=99)
+    g = oracle_mod.backward(spec, inp, dout, 0.2, 0.05)
+    dWg, dbg = oracle_mod.backward_gate(spec, inp, dout, 0.2, 0.05)
+    assert np.array_equal(dWg, g["dWg"]) and np.array_equal(dbg, g["dbg"])
+    lg = oracle_mod.logits(spec, inp["x"], inp["Wg"], inp["bg"]) * 1.5
+    g = oracle_mod.backward(spec, inp, dout, 0.1, 0.3, given_logits=lg)
+    dWg, dbg = oracle_mod.backward_gate(spec, inp, dout, 0.1, 0.3, given_logits=lg)
+    assert np.array_equal(dWg, g["dWg"]) and np.array_equal(dbg, g["dbg"])
