@@ -17,7 +17,9 @@
  * - Pointers are DEVICE pointers unless marked (host).  The caller owns every
  *   buffer; the library never allocates, frees, or keeps a pointer after a
  *   call returns, and holds no state, so calls on distinct streams with
- *   distinct workspaces may run concurrently.
+ *   distinct workspaces may run concurrently.  The one exception is
+ *   moe_forward_noalloc, whose workspace is a fixed device array of the
+ *   library (see there).
  * - Every GPU call is asynchronous on `stream` and never synchronises with
  *   the host, so a call sequence can be captured into a HIP graph.
  * - Row-major storage.  x[T][H]; gate Wg[H][E]; W1[E][H][F]; W2[E][F][H]:
@@ -178,6 +180,27 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg,
                          int32_t* topk_idx, float* topk_w, int32_t* counts,
                          int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
                          hipStream_t stream, hipEvent_t* stage_events);
+
+/* moe_forward with a workspace the library owns, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results as
+ * moe_forward without ws / ws_bytes: the workspace is a fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends (its device address is looked up on the first call on that
+ * device).  Problems whose moe_workspace_bytes() exceeds it return
+ * MOE_ERR_WORKSPACE before anything is enqueued (64 MiB holds the
+ * Mixtral-shaped layer up to 448 tokens).  No call allocates or frees
+ * anything.  Every call on one GPU uses the same array: calls that overlap on
+ * one GPU (two streams, two threads) race and give undefined results;
+ * serialise them.  Nothing needs clearing between calls: each forward writes
+ * every scratch region before reading it. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* Wg,
+                                 const void* bg, const void* W1, const void* b1, const void* W2,
+                                 const void* b2, void* out, float* losses, float* logits,
+                                 int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                 int32_t* offsets, int32_t* pos, hipStream_t stream,
+                                 hipEvent_t* stage_events);
 
 /* ------------------------------------------------------------ expert choice
  * Expert-choice routing (Core Concepts, 2. Routing Mechanisms: the experts

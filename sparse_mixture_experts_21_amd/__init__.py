@@ -36,7 +36,8 @@ EXPORTS = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_status_string",
            "moe_ec_capacity", "moe_ec_workspace_bytes", "moe_route_expert_choice",
            "moe_forward_expert_choice", "moe_train_workspace_bytes", "moe_forward_train",
-           "moe_backward")
+           "moe_backward", "moe_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp, vp]
+        L.moe_forward_noalloc.argtypes = [P] + [vp] * 17
         i64 = ctypes.c_int64
         L.moe_ec_capacity.argtypes = [P, i64, ctypes.POINTER(i64)]
         L.moe_ec_workspace_bytes.argtypes = [P, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -112,7 +114,7 @@ def lib() -> ctypes.CDLL:
                   "moe_expert_ffn", "moe_combine", "moe_forward", "moe_ec_capacity",
                   "moe_ec_workspace_bytes", "moe_route_expert_choice",
                   "moe_forward_expert_choice", "moe_train_workspace_bytes",
-                  "moe_forward_train", "moe_backward"):
+                  "moe_forward_train", "moe_backward", "moe_forward_noalloc"):
             getattr(L, f).restype = st
         L.moe_status_string.argtypes = [st]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -207,6 +209,18 @@ def moe_forward(p: Problem, x, Wg, bg, W1, b1, W2, b2, out, losses, ws, logits=N
                              _ptr(pos), _ptr(ws), _nbytes(ws), _stream(stream, out),
                              ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None),
            "moe_forward")
+
+
+def moe_forward_noalloc(p: Problem, x, Wg, bg, W1, b1, W2, b2, out, losses, logits=None,
+                        topk_idx=None, topk_w=None, counts=None, offsets=None, pos=None,
+                        stream=None, events: Optional["StageEvents"] = None) -> None:
+    ev = events.array() if events is not None else None
+    _check(lib().moe_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1),
+                                     _ptr(b1), _ptr(W2), _ptr(b2), _ptr(out), _ptr(losses),
+                                     _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                                     _ptr(offsets), _ptr(pos), _stream(stream, out),
+                                     ctypes.cast(ev, ctypes.c_void_p) if ev is not None
+                                     else None), "moe_forward_noalloc")
 
 
 def moe_ec_capacity(p: Problem, group: int) -> int:

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -262,6 +263,48 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// The workspace of moe_forward_noalloc: a file-scope device array that every
+// GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is looked up once per device (with that device current) and only
+// that address is handed to kernels.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream`.
+hipError_t scratch_address(hipStream_t stream, char** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return e;
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = static_cast<char*>(g_scratch_dev[dev]);
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +425,34 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
     return forward_impl(*p, L, static_cast<char*>(ws), x, Wg, bg, W1, b1, W2, b2, out, losses,
                         logits, topk_idx, topk_w, counts, offsets, pos, nullptr, stream,
                         stage_events);
+}
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const void* Wg,
+                                 const void* bg, const void* W1, const void* b1, const void* W2,
+                                 const void* b2, void* out, float* losses, float* logits,
+                                 int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                 int32_t* offsets, int32_t* pos, hipStream_t stream,
+                                 hipEvent_t* stage_events) {
+    moe_status_t st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!x || !Wg || !W1 || !W2 || !out || !losses) return MOE_ERR_INVALID_ARG;
+    if (stage_events) {
+        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    }
+    if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
+        !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !aligned16(losses) ||
+        !opt_ok(logits) || !opt_ok(topk_idx) || !opt_ok(topk_w) || !opt_ok(counts) ||
+        !opt_ok(offsets) || !opt_ok(pos))
+        return MOE_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(*p);
+    if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    char* w = nullptr;
+    if (scratch_address(stream, &w) != hipSuccess) return MOE_ERR_HIP;
+    // every region of the workspace is written before it is read within one
+    // forward, so the previous call's contents need no clearing
+    return forward_impl(*p, L, w, x, Wg, bg, W1, b1, W2, b2, out, losses, logits, topk_idx,
+                        topk_w, counts, offsets, pos, nullptr, stream, stage_events);
 }
 
 moe_status_t moe_ec_capacity(const moe_problem_t* p, int64_t group, int64_t* C) {

@@ -370,3 +370,37 @@ def test_train_workspace_sizes_and_nan_weights():
     assert bwd(p, g_aux=math.nan) == moe.MOE_ERR_INVALID_ARG
     arr = (ctypes.c_void_p * moe.MOE_BACKWARD_EVENTS)()
     assert bwd(p, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- fixed scratch
+def fwd_noalloc(p, **kw):
+    a = dict(x=A, Wg=A, bg=None, W1=A, b1=None, W2=A, b2=None, out=A, losses=A, logits=None,
+             idx=None, w=None, counts=None, off=None, pos=None, ev=None)
+    a.update(kw)
+    return moe.lib().moe_forward_noalloc(ctypes.byref(p), a["x"], a["Wg"], a["bg"], a["W1"],
+                                         a["b1"], a["W2"], a["b2"], a["out"], a["losses"],
+                                         a["logits"], a["idx"], a["w"], a["counts"], a["off"],
+                                         a["pos"], None, a["ev"])
+
+
+@pytest.mark.parametrize("kw,status", BAD_PROBLEMS, ids=[str(b[0]) for b in BAD_PROBLEMS])
+def test_noalloc_bad_problem_rejected(kw, status):
+    assert fwd_noalloc(P(**kw)) == status
+
+
+@pytest.mark.parametrize("arg", ["x", "Wg", "W1", "W2", "out", "losses"])
+def test_noalloc_null_and_misaligned(arg):
+    assert fwd_noalloc(P(), **{arg: None}) == moe.MOE_ERR_INVALID_ARG
+    assert fwd_noalloc(P(), **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_limit_and_null_event():
+    """A problem whose workspace exceeds the fixed scratch is refused with
+    MOE_ERR_WORKSPACE before any HIP call (this runs without a GPU)."""
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
+    big = P(T=8192, H=1024, E=8, k=2, F=4096)
+    assert moe.moe_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(big) == moe.MOE_ERR_WORKSPACE
+    arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
+    assert fwd_noalloc(P(), ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
