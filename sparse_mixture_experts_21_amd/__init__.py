@@ -18,7 +18,9 @@ import os
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIB may name another build of the same sources (the host-sanitizer build
+# that the CPU tests load); the default is the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1

@@ -62,5 +62,54 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+# Host-sanitizer build: moe_api.cpp (argument validation, workspace layout,
+# launch sequencing) with AddressSanitizer and UndefinedBehaviorSanitizer on
+# its host code only, linked with the regular kernel objects into
+# libmoe_hostsan.so.  The CPU tests load it through MOE_LIB with the clang
+# ASan runtime preloaded (asan_runtime()).
+SAN_LIB = os.path.join(PKG, "libmoe_hostsan.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that a process loading libmoe_hostsan.so preloads."""
+    import glob
+    root = os.path.dirname(os.path.dirname(hipcc())) if os.path.isabs(hipcc()) else "/opt/rocm"
+    hits = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under the ROCm llvm tree")
+    return hits[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    others = [os.path.join(OBJDIR, os.path.splitext(f)[0] + ".o") for f in SOURCES
+              if f != "moe_api.cpp"]
+    if not all(os.path.exists(o) for o in others):
+        build(verbose)
+    os.makedirs(OBJDIR, exist_ok=True)
+    obj = os.path.join(OBJDIR, "moe_api_hostsan.o")
+    cmd = [hipcc()] + COMMON + ["-g"] + SAN_HOST + ["-c", os.path.join(CSRC, "moe_api.cpp"),
+                                                    "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on moe_api.cpp (host sanitizers):\n{r.stderr}")
+    tmp = SAN_LIB + f".tmp{os.getpid()}"
+    # the sanitizer runtime is not linked in: its symbols resolve against the
+    # preloaded clang ASan runtime (which carries the UBSan handlers too)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj] + others
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -310,7 +310,12 @@ hipError_t scratch_address(hipStream_t stream, char** out) {
 extern "C" {
 
 const char* moe_status_string(moe_status_t s) {
-    switch (s) {
+    // a C caller may pass any int: read the raw value (in C++ a value outside
+    // the enumerators would be undefined behaviour)
+    static_assert(sizeof(moe_status_t) == sizeof(int), "status is int-sized");
+    int v = 0;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
         case MOE_OK: return "ok";
         case MOE_ERR_INVALID_ARG: return "invalid argument";
         case MOE_ERR_UNSUPPORTED: return "unsupported problem (outside the kernel envelope)";
