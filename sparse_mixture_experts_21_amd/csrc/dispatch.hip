@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64) void chunk_rank(const int32_t* __restrict__ top
     __syncthreads();
     if (c == 0) {
         for (int e = lane; e <= E; e += 64) offsets[e] = off[e];
-        if (FIN && lane == 0) fin_losses(fin, E);
+        if (FIN) fin_losses(fin, E);
     }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int64_t j0 = c * kChunkTok * k;

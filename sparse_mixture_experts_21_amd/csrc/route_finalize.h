@@ -7,7 +7,7 @@
 // adds blocks 4t .. 4t + 3 of each round of 1024 in order in fp64, then a
 // butterfly over the wave and the 4 wave sums in order.  The order is fixed,
 // so the losses are bitwise reproducible without floating-point atomics.  The
-// column sums go to the workspace; one thread then forms the losses.  Used by
+// column sums go to the workspace; one wave then forms the losses.  Used by
 // the router's own finalize kernels and, inside the fused forward, by the
 // dispatch scan and rank kernels.
 #pragma once
@@ -83,15 +83,36 @@ __device__ inline void fin_column_block(const FinArgs& f, int E, int c) {
     }
 }
 
-// One thread, once every column sum is in the workspace.
+// One whole wave (64 lanes, all calling), once every column sum is in the
+// workspace: lane l takes experts l, l + 64, ... (E <= 256), all loads issued
+// together, its terms added in expert order, then a butterfly over the wave
+// (each level adds the same two operands on both lanes, so every lane ends
+// with the same bits); lane 0 writes the losses.
 __device__ inline void fin_losses(const FinArgs& f, int E) {
-    double acc = 0.0;
-    for (int e = 0; e < E; ++e) {
-        f.counts[e] = (int32_t)f.col_cnt[e];
-        acc += ((double)f.col_cnt[e] / (double)(f.T * f.k)) * (f.col_sum[e] / (double)f.T);
+    const int lane = threadIdx.x & 63;
+    long long cnt[4];
+    double sum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                 // unconditional loads at clamped indices
+        const int e = min(lane + 64 * i, E - 1);
+        cnt[i] = f.col_cnt[e];
+        sum[i] = f.col_sum[e];
     }
-    f.losses[0] = (float)((double)E * acc);
-    f.losses[1] = (float)(f.col_sum[E] / (double)f.T);
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            f.counts[e] = (int32_t)cnt[i];
+            acc += ((double)cnt[i] / (double)(f.T * f.k)) * (sum[i] / (double)f.T);
+        }
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) acc += __shfl_xor(acc, d);
+    if (lane == 0) {
+        f.losses[0] = (float)((double)E * acc);
+        f.losses[1] = (float)(f.col_sum[E] / (double)f.T);
+    }
 }
 
 }  // namespace moe

@@ -3,16 +3,12 @@
 // the router z-loss ("moe-training" SKILL page, Quick Start, Basic MoE
 // Architecture; Core Concepts, 3. Load Balancing).
 //
-// One workgroup (4 waves) owns 16 tokens.  The gate linear is a skinny GEMM
-// [16 x H] . [H x E] on v_mfma_f32_16x16x32_bf16; the 4 waves split the H axis
-// and wave 0 adds the other waves' partial tiles, parked in LDS, in a fixed
-// order.  With E <= 16 (route_bf16_ring) x and the gate stream through an LDS
-// ring by direct DMA; wider gates (route_bf16) load 16-byte fragments straight
-// into registers from x and from a per-call [E][H] copy of the gate.  The
-// routing epilogue runs 4 lanes per token.  Per-block partials (sum of softmax
-// probabilities per expert, sum of lse^2, expert histogram) are reduced in a
-// fixed order by one workgroup per column, so the losses are bitwise
-// reproducible without floating-point atomics.
+// bf16: route_bf16 (below) streams x and the gate through LDS and computes the
+// gate tile of TM tokens on MFMA, then the routing epilogue.  fp32: plain FMA
+// dot products and a 4-lanes-per-token epilogue.  Per-block partials (sum of
+// softmax probabilities per expert, sum of lse^2, expert histogram, per 16
+// tokens) are reduced in a fixed order by one workgroup per column, so the
+// losses are bitwise reproducible without floating-point atomics.
 #include "moe_internal.h"
 #include "lds_dma.h"
 #include "route_finalize.h"
@@ -22,17 +18,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-// cache-policy operand of a buffer load: nontemporal (x is read once here)
-constexpr int kNtLoad = 2;
-
-// ---------------------------------------------------------------- gate transpose
-__global__ void gate_transpose_bf16(const uint16_t* __restrict__ Wg, uint16_t* __restrict__ WgT,
-                                    int H, int E) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)H * E) return;
-    int h = (int)(i / E), e = (int)(i % E);
-    WgT[(int64_t)e * H + h] = Wg[i];
-}
 
 // ---------------------------------------------------------------- routing epilogue
 // logit_s: [16][E] fp32 logits of the block's tokens (bias already added).
@@ -124,325 +109,417 @@ __device__ void route_epilogue(float* logit_s, int32_t* idx_s, float* lse_s, int
     }
 }
 
-// ---------------------------------------------------------------- routing epilogue, E <= 16
-// Thread t owns (token r = t / 16, expert e = t % 16): the 16 lanes of a token
-// are one aligned group of a wave.  red[w][r][e] holds wave w's partial gate
-// tile; the logit is ((w0 + w1) + w2) + w3 (+ bias).  Max, softmax sum and the
-// renormalisation sum are butterflies within the group: every lane adds the
-// same two operands at every level (in either order, which is exact), so all
-// 16 lanes agree bit for bit.  The top-k slot of an expert is its rank among
-// the token's logits, descending, equal values -> lower index first.  Block
-// partials: per expert over the block's tokens (4 per wave by shuffles, then
-// waves 0..3 in order through LDS), written column-major [E][nblk].
-__device__ __forceinline__ void route_epilogue16(float* red, int64_t t0, int ntok, int E, int k,
-                                                 const uint16_t* __restrict__ bg,
-                                                 float* __restrict__ logits_out,
-                                                 const RouteOut& o) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = tid >> 4, e = tid & 15, grp = lane & ~15;
-    const bool ev = e < E, tv = r < ntok;
-    float l = ((red[(0 * kRouteTok + r) * 16 + e] + red[(1 * kRouteTok + r) * 16 + e]) +
-               red[(2 * kRouteTok + r) * 16 + e]) + red[(3 * kRouteTok + r) * 16 + e];
-    if (ev && bg) l += __uint_as_float((uint32_t)bg[e] << 16);
-    if (ev && tv && logits_out) logits_out[(t0 + r) * E + e] = l;
-    float m = ev ? l : -INFINITY;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
-    const float pu = ev ? expf(l - m) : 0.f;                    // unnormalised probability
-    float Z = pu;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) Z += __shfl_xor(Z, d);
-    int rank = 0;
-    for (int j = 0; j < E; ++j) {
-        const float lj = __shfl(l, grp | j);
-        rank += (lj > l) || (lj == l && j < e);
-    }
-    const bool sel = ev && rank < k;
-    // renormalised top-k weight: exp(l_e - m) / sum over the selected of exp(l - m)
-    float S = sel ? pu : 0.f;
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) S += __shfl_xor(S, d);
-    if (sel && tv) {
-        o.topk_idx[(t0 + r) * k + rank] = e;
-        o.topk_w[(t0 + r) * k + rank] = pu / S;
-    }
-    // block partials
-    float ps = (ev && tv) ? pu / Z : 0.f;
-    int cnt = (sel && tv) ? 1 : 0;
-    float l2 = 0.f;
-    if (e == 0 && tv) {
-        const float lse = m + logf(Z);
-        l2 = lse * lse;
-    }
-#pragma unroll
-    for (int d = 16; d < 64; d <<= 1) {
-        ps += __shfl_xor(ps, d);
-        cnt += __shfl_xor(cnt, d);
-        l2 += __shfl_xor(l2, d);
-    }
-    __syncthreads();                         // every lane has read red
-    float* part = red;                       // [4 waves][16] probability sums
-    int* part_c = reinterpret_cast<int*>(red + 4 * 16);
-    float* part_l = red + 8 * 16;            // [4 waves]
-    if (lane < 16) {
-        part[wave * 16 + lane] = ps;
-        part_c[wave * 16 + lane] = cnt;
-        if (lane == 0) part_l[wave] = l2;
-    }
-    __syncthreads();
-    const int64_t blk = blockIdx.x, nblk = gridDim.x;
-    if (tid < E) {
-        o.blk_psum[tid * nblk + blk] = ((part[tid] + part[16 + tid]) + part[32 + tid]) + part[48 + tid];
-        o.blk_cnt[tid * nblk + blk] = part_c[tid] + part_c[16 + tid] + part_c[32 + tid] + part_c[48 + tid];
-    }
-    if (tid == 0) o.blk_lse2[blk] = ((part_l[0] + part_l[1]) + part_l[2]) + part_l[3];
-}
-
 // ---------------------------------------------------------------- bf16 router
-// NT = number of 16-expert tiles (E <= 16 NT).  Waves 1..3 park their partial
-// tiles in LDS red[3][16][16 NT]; wave 0 adds them to its own registers in the
-// fixed order ((w0 + w1) + w2) + w3 and writes logit_s[16][E].
-template <int NT>
-__global__ __launch_bounds__(kThreads) void route_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT,
-    const uint16_t* __restrict__ bg, float* __restrict__ logits_io, int logits_in, int64_t T,
-    int H, int E, int k, RouteOut o) {
-    constexpr int E16 = NT * 16;
-    __shared__ float logit_s[kRouteTok * E16];          // [16][E] (row stride E)
-    __shared__ float red[3 * kRouteTok * E16];          // [3][16][E16]
-    __shared__ int32_t idx_s[kRouteTok * kMaxK];
-    __shared__ float lse_s[kRouteTok];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t t0 = (int64_t)blockIdx.x * kRouteTok;
-
-    if (!logits_in) {
-        const int row = lane & 15, g = lane >> 4;
-        // x through a raw buffer resource based at the block's first token
-        // (loads at offsets past the end return zero) and the transposed gate
-        // likewise; every lane owns 8 consecutive h of token min(t0+row, T-1).
-        const uint32_t xrow = (uint32_t)(min(t0 + row, T - 1) - t0) * (uint32_t)H * 2u;
-        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            uniform_ptr(x + t0 * H), (short)0,
-            (T - t0 < kRouteTok ? (int)(T - t0) : kRouteTok) * H * 2,
-            0x00020000);
-        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            uniform_ptr(WgT), (short)0, E * H * 2, 0x00020000);
-        f32x4_t acc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // wave w reduces the contiguous k-steps [ks0, ks1) of 32 h each, UNR at a
-        // time with all of their loads in flight before the MFMAs
-        const int nks = (H + 31) >> 5;
-        const int wv = __builtin_amdgcn_readfirstlane(wave);   // uniform loop bounds
-        const int ks0 = (wv * nks) / kWaves, ks1 = ((wv + 1) * nks) / kWaves;
-        constexpr int UNR = NT <= 2 ? 8 : (NT <= 4 ? 4 : 2);
-        for (int ks = ks0; ks < ks1; ks += UNR) {
-            u32x4_t av[UNR], bv[UNR][NT];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int h0 = (ks + u) * 32 + g * 8;
-                // H % 8 == 0, so a lane's 8 h are all in range or all past the end
-                const bool ok = (ks + u) < ks1 && h0 < H;
-                av[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xr, ok ? xrow + (uint32_t)h0 * 2u : 0x80000000u, 0, kNtLoad);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int e = nt * 16 + row;
-                    const uint32_t off = (ok && e < E) ? ((uint32_t)e * (uint32_t)H + (uint32_t)h0) * 2u
-                                                       : 0x80000000u;
-                    bv[u][nt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, av[u]), __builtin_bit_cast(bf16x8_t, bv[u][nt]),
-                        acc[nt], 0, 0, 0);
-        }
-        // D[token][expert]: lane holds tokens 4*(lane/16)+i of expert nt*16 + lane%16
-        if (wave > 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[((wave - 1) * kRouteTok + (lane >> 4) * 4 + i) * E16 + nt * 16 +
-                        (lane & 15)] = acc[nt][i];
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int e = nt * 16 + (lane & 15);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = (lane >> 4) * 4 + i;
-                    float v = acc[nt][i];
-                    v += red[(0 * kRouteTok + r) * E16 + e];
-                    v += red[(1 * kRouteTok + r) * E16 + e];
-                    v += red[(2 * kRouteTok + r) * E16 + e];
-                    if (e < E) {
-                        if (bg) v += __uint_as_float((uint32_t)bg[e] << 16);
-                        logit_s[r * E + e] = v;
-                        if (logits_io && t0 + r < T) logits_io[(t0 + r) * E + e] = v;
-                    }
-                }
-            }
-        }
-    } else {
-        for (int j = tid; j < kRouteTok * E; j += kThreads) {
-            const int r = j / E;
-            logit_s[j] = (t0 + r < T) ? logits_io[(t0 + r) * E + (j % E)] : 0.f;
-        }
-    }
-    __syncthreads();
-    route_epilogue(logit_s, idx_s, lse_s, t0, T, E, k, o);
-}
-
-// ---------------------------------------------------------------- bf16 router, E <= 16
-// The block's 16 token rows stream through an LDS ring of kRingStages stages of
-// kStageH hidden units, next to the matching slab Wg[h0 .. h0 + kStageH)[0 .. E)
-// of the gate (E KB, contiguous in the [H][E] layout, so no transposed copy is
-// needed).  One direct-to-LDS DMA moves 1 KB, so x leaves HBM in whole
-// contiguous row segments: fragment-shaped register loads touch 16 rows x 64 B
-// per instruction, which HBM serves well below its streaming rate.  x is read
-// with the nontemporal hint: it is streamed once here, and a normal load would
-// first have to write back the dirty lines earlier kernels left in the
-// last-level cache.  The 16-byte chunk c of token row r sits at slot c ^ r, so
-// the 16 rows of a fragment read land on distinct banks; a lane assembles its
-// gate fragment (8 consecutive h of one expert) from 16-bit reads of the slab.
-// The waves split each stage's 16 k-steps.  Stage bookkeeping: before
-// computing stage s a wave waits until only the DMAs of the (kRingStages - 2)
-// younger stages are outstanding; a barrier then publishes every wave's part of
-// stage s and frees the slot of stage s - 1, which the DMAs of stage
-// s + kRingStages - 1 overwrite.
-#ifndef MOE_RING_RB
-#define MOE_RING_RB 512
-#endif
-#ifndef MOE_RING_NS
-#define MOE_RING_NS 4
-#endif
-constexpr int kRingStages = MOE_RING_NS;
-constexpr int kRowBytes = MOE_RING_RB;    // bytes of one token row per stage
-
-template <int EC>   // gate columns reserved per stage (E <= EC)
-struct RingCfg {
-    static constexpr int RB = kRowBytes, NS = kRingStages;
-    static constexpr int SH = RB / 2;                       // hidden units per stage
-    static constexpr int RPU = 1024 / RB;                   // token rows per 1 KB DMA
-    static constexpr int XU = kRouteTok / RPU;              // DMAs for the token rows
-    static constexpr int WU = EC * RB / 1024;               // DMAs for the gate slab (max)
-    static constexpr int ND = (XU + WU) / kWaves;           // DMAs per wave per stage
-    static constexpr int STAGE = (XU + WU) * 1024;
-    static constexpr int LDS = NS * STAGE + 1024;           // + a sink for padding DMAs
-    static constexpr int KW = SH / 32 / kWaves;             // k-steps per wave per stage
-    static_assert((XU + WU) % kWaves == 0 && KW >= 1, "ring shape");
-    static_assert(NS >= 3, "the wait count assumes two younger stages may be in flight");
+// One workgroup (4 waves) owns TM consecutive tokens and computes their gate
+// tile [TM][E] = x[TM][H] . Wg[H][E] on v_mfma_f32_16x16x32_bf16 (A = 16 token
+// rows, B = 16 experts, 32 hidden units per k-step), streaming x and the gate
+// through a ring of NS LDS stages of BK hidden units by direct DMA (1 KB per
+// wave instruction, x nontemporal: it is read once, and a plain load would
+// first write back the dirty lines earlier kernels left in the last-level
+// cache).  x rows keep whole contiguous row segments per DMA; the gate slab
+// Wg[h0 .. h0 + BK)[0 .. E) is contiguous in the [H][E] layout, so neither
+// needs a copy.  In LDS, 16-byte chunk c of token row r sits at slot
+// c ^ f(r) (f below), so the 16 rows of an A fragment hit 16 distinct bank
+// slots.  A B fragment (8 consecutive h of one expert per lane) comes from
+// the slab with two transposing reads (ds_read_b64_tr_b16: in each 16-lane
+// group, source lane s reads 4 experts of row h0 + s / 4 and lane i receives
+// rows h0 .. h0 + 3 of expert i) when E % 4 == 0 (8-byte aligned rows), else
+// from eight 16-bit reads.
+//
+// Work split: with E <= 64 the waves split each stage's k-steps (every wave
+// accumulates the whole [TM][E] tile over its own k-steps) and the four
+// partial tiles are added in the fixed order ((w0 + w1) + w2) + w3; with
+// wider gates each wave owns every fourth 16-expert tile over all k-steps.
+//
+// Routing epilogue.  E <= 16 (16 tokens per workgroup): one thread per
+// (token, expert), the 16 lanes of a token an aligned group: max and softmax
+// sum by butterflies (the same operands on every lane of the group), top-k
+// slot = the expert's rank among the token's logits (descending, equal
+// logits -> lower expert).  Wider gates: LPT = 256 / TM lanes per token, lane
+// q taking experts q, q + LPT, ..., top-k by k passes of a first-maximum
+// argmax over the untaken experts.  Both renormalise the k selected
+// probabilities.  Per 16-token block (the dispatch chunk): the sums of
+// softmax probabilities and the expert counts (tokens in a fixed order) and
+// the sum of lse^2, column-major [E][nblk], for the fixed-order loss
+// reduction.
+template <int EB>   // 16-expert tiles: E <= 16 EB
+struct RouteCfg {
+    static constexpr bool kSplitE = EB >= 8;              // waves own expert tiles
+    static constexpr int TM = EB == 1 ? 16 : 32;          // tokens per workgroup
+    static constexpr int BK = EB == 1 ? 256 : EB <= 8 ? 128 : 64;     // h per stage
+    static constexpr int NS = EB >= 8 ? 2 : 3;            // LDS stages
+    static constexpr int E16 = 16 * EB;
+    static constexpr int P = BK * 2;                      // bytes of a token row per stage
+    static constexpr int CPR = P / 16;                    // 16-byte chunks per row
+    static constexpr int XU = TM * P / 1024;              // 1 KB DMAs for the token rows
+    static constexpr int WUMAX = (BK * E16 * 2 + 1023) / 1024;   // ... for the gate slab
+    static constexpr int ND = (XU + WUMAX + 3) / 4;       // DMAs per wave per stage
+    static constexpr int STAGE = (XU + WUMAX) * 1024;
+    static constexpr int KS = BK / 32;                    // k-steps per stage
+    static constexpr int KW = kSplitE ? KS : KS / 4;      // k-steps per wave per stage
+    static constexpr int TT = TM / 16;                    // token tiles
+    static constexpr int ET = kSplitE ? EB / 4 : EB;      // expert tiles per wave
+    static constexpr int LPT = 256 / TM;                  // epilogue lanes per token
+    // epilogue LDS: split-K partial tiles [4][TM][E16] (or none), logits
+    // [TM][E16], selection flags [TM][E16], lse^2 [TM]
+    static constexpr int RED = kSplitE ? 0 : 4 * TM * E16 * 4;
+    static constexpr int EPI = RED + TM * E16 * 4 + TM * E16 + TM * 4;
+    static constexpr int RING = NS * STAGE + 1024;        // + a sink for padding DMAs
+    static constexpr int LDS = RING > EPI ? RING : EPI;
+    static_assert(TM * P % 1024 == 0 && 1024 % P == 0, "whole rows per DMA");
+    static_assert(kSplitE ? EB % 4 == 0 : KS % 4 == 0, "work split");
+    static_assert(EB != 1 || TM == 16, "the 16-lane epilogue takes 16 tokens");
 };
 
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-template <int EC>
-__global__ __launch_bounds__(kThreads) void route_bf16_ring(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg,
-    const uint16_t* __restrict__ bg, float* __restrict__ logits_out, int64_t T, int H, int E,
-    int k, RouteOut o) {
-    using C = RingCfg<EC>;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[C::LDS];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t t0 = (int64_t)blockIdx.x * kRouteTok;
-    const int ntok = (T - t0 < kRouteTok) ? (int)(T - t0) : kRouteTok;
-    const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(x + t0 * H), (uint32_t)(ntok * H * 2));
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(uniform_ptr(Wg), (uint32_t)(E * H * 2));
-    const int nst = (H + C::SH - 1) / C::SH;
-    const int wu = (E * C::RB + 1023) / 1024;          // gate-slab DMAs actually needed
-
-    // DMA q of this wave fills 1 KB unit j = wave + 4 q of the stage: token rows
-    // (RPU per unit) first, then the gate slab; units past XU + wu are padding
-    // DMAs into the sink (every wave issues C::ND per stage, which keeps the
-    // vmcnt bookkeeping static).
-    auto issue = [&](int st) {
-        const uint32_t slot = ring0 + (uint32_t)((st % C::NS) * C::STAGE);
-#pragma unroll
-        for (int q = 0; q < C::ND; ++q) {
-            const int j = wave + kWaves * q;
-            uint32_t dst = ring0 + (uint32_t)(C::NS * C::STAGE);
-            if (j < C::XU) {
-                const int r = j * C::RPU + lane / (64 / C::RPU);
-                const int cl = lane % (64 / C::RPU);
-                const int h = st * C::SH + 8 * (cl ^ (r & 15));
-                const uint32_t off = (st < nst && h < H)
-                    ? ((uint32_t)r * (uint32_t)H + (uint32_t)h) * 2u : kOob;
-                dst = slot + (uint32_t)(j * 1024);
-                dma16_nt(xr, off, __builtin_amdgcn_readfirstlane(dst));
-            } else {
-                // slab bytes past E * H * 2 (h >= H) are out of the resource: zero
-                uint32_t off = kOob;
-                if (j < C::XU + wu) {
-                    dst = slot + (uint32_t)(j * 1024);
-                    if (st < nst)
-                        off = (uint32_t)st * (uint32_t)(E * C::RB) +
-                              (uint32_t)((j - C::XU) * 1024) + (uint32_t)lane * 16u;
-                }
-                dma16(wr, off, __builtin_amdgcn_readfirstlane(dst));
-            }
-        }
-    };
-
-    const int row = lane & 15, g = lane >> 4;
-    const int er = row < E ? row : E - 1;            // columns >= E are discarded
-    const bool row_ok = row < ntok;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < C::NS - 1; ++st) issue(st);
-    for (int st = 0; st < nst; ++st) {
-        wait_vmcnt<(C::NS - 2) * C::ND>();
-        lds_barrier();
-        issue(st + C::NS - 1);
-        const uint32_t slot = ring0 + (uint32_t)((st % C::NS) * C::STAGE);
-        const uint32_t slab = slot + (uint32_t)(C::XU * 1024);
-#pragma unroll
-        for (int kq = 0; kq < C::KW; ++kq) {
-            const int kk = wave * C::KW + kq;
-            const int c = 4 * kk + g;                 // 16-byte chunk of the stage row
-            const bool h_ok = st * C::SH + 8 * c < H;
-            u32x4_t a = *reinterpret_cast<const lds_u32x4_t*>(
-                (uintptr_t)(slot + (uint32_t)(row * C::RB + ((c ^ row) << 4))));
-            const lds_u16_t* pw = reinterpret_cast<const lds_u16_t*>(
-                (uintptr_t)(slab + (uint32_t)((8 * c * E + er) * 2)));
-            u32x4_t b;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                b[i] = (uint32_t)pw[(2 * i) * E] | ((uint32_t)pw[(2 * i + 1) * E] << 16);
-            const u32x4_t z = {0u, 0u, 0u, 0u};
-            if (!(h_ok && row_ok)) a = z;
-            if (!h_ok) b = z;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          __builtin_bit_cast(bf16x8_t, b), acc,
-                                                          0, 0, 0);
-        }
-    }
-    wait_vmcnt<0>();
-    lds_barrier();
-    float* red = reinterpret_cast<float*>(ring);                 // [4 waves][16][16]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        red[(wave * kRouteTok + (lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[i];
-    __syncthreads();
-    route_epilogue16(red, t0, ntok, E, k, bg, logits_out, o);
+// swizzle of token row r: 16 consecutive rows land on 16 distinct bank slots
+template <int CPR>
+__device__ __forceinline__ int row_swz(int r) {
+    if constexpr (CPR >= 16) return r & 15;
+    else if constexpr (CPR == 8) return (r >> 1) & 7;
+    else return (r >> 2) & 3;
 }
 
+template <int EB>
+__global__ __launch_bounds__(kThreads) void route_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg,
+    const uint16_t* __restrict__ bg, float* __restrict__ logits_io, int logits_in, int64_t T,
+    int H, int E, int k, RouteOut o) {
+    using C = RouteCfg<EB>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t0 = (int64_t)blockIdx.x * C::TM;
+    const int ntok = (T - t0 < C::TM) ? (int)(T - t0) : C::TM;
+    float* red = reinterpret_cast<float*>(lds);                      // [4][TM][E16]
+    float* lg = reinterpret_cast<float*>(lds + C::RED);              // [TM][E16]
+    uint8_t* flag = lds + C::RED + C::TM * C::E16 * 4;               // [TM][E16]
+    float* lse_s = reinterpret_cast<float*>(flag + C::TM * C::E16);  // [TM]
+    const int row = lane & 15, g = lane >> 4;
 
-template <int NT>
-static void launch_route_bf16_nt(int64_t nblk, hipStream_t s, const uint16_t* x,
-                                 const uint16_t* WgT, const uint16_t* bg, float* logits,
-                                 int logits_in, int64_t T, int H, int E, int k, RouteOut o) {
-    route_bf16<NT><<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(x, WgT, bg, logits,
-                                                                     logits_in, T, H, E, k, o);
+    if (!logits_in) {
+        const uint32_t ring0 = (uint32_t)(uintptr_t)lds;
+        const __amdgpu_buffer_rsrc_t xr =
+            make_rsrc(uniform_ptr(x + t0 * H), (uint32_t)ntok * (uint32_t)H * 2u);
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(uniform_ptr(Wg), (uint32_t)(E * H * 2));
+        const int nst = (H + C::BK - 1) / C::BK;
+        const int wu = (C::BK * E * 2 + 1023) / 1024;            // gate DMAs actually needed
+        // DMA q of this wave fills 1 KB unit j = wave + 4 q of the stage: the
+        // token rows first, then the gate slab; units past XU + wu go to the
+        // sink (every wave issues ND per stage: static vmcnt bookkeeping).
+        auto issue = [&](int st) {
+            const uint32_t slot = ring0 + (uint32_t)((st % C::NS) * C::STAGE);
+#pragma unroll
+            for (int q = 0; q < C::ND; ++q) {
+                const int j = wave + 4 * q;
+                uint32_t dst = ring0 + (uint32_t)(C::NS * C::STAGE);
+                if (j < C::XU) {
+                    constexpr int LPR = C::CPR < 64 ? C::CPR : 64;      // lanes per row
+                    const int r = j * (64 / LPR) + lane / LPR;
+                    const int cs = lane % LPR;                           // slot chunk
+                    const int h = st * C::BK + 8 * (cs ^ row_swz<C::CPR>(r));
+                    const uint32_t off = (st < nst && h < H)
+                        ? ((uint32_t)r * (uint32_t)H + (uint32_t)h) * 2u : kOob;
+                    dst = slot + (uint32_t)(j * 1024);
+                    dma16_nt(xr, off, __builtin_amdgcn_readfirstlane(dst));
+                } else {
+                    // slab bytes past E * H * 2 (h >= H) are outside the resource: zero
+                    uint32_t off = kOob;
+                    if (j < C::XU + wu) {
+                        dst = slot + (uint32_t)(j * 1024);
+                        if (st < nst)
+                            off = (uint32_t)st * (uint32_t)(C::BK * E * 2) +
+                                  (uint32_t)((j - C::XU) * 1024) + (uint32_t)lane * 16u;
+                    }
+                    dma16(wr, off, __builtin_amdgcn_readfirstlane(dst));
+                }
+            }
+        };
+
+        f32x4_t acc[C::TT][C::ET];
+#pragma unroll
+        for (int a = 0; a < C::TT; ++a)
+#pragma unroll
+            for (int b = 0; b < C::ET; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // B-fragment addresses (bytes into the slab, + the k-step's 32 E rows).
+        // Transposing reads (E % 4 == 0): source lane row = lane % 16 / 4 of
+        // its 4-row group, 4 experts from 16 t + 4 (lane % 4); experts past E
+        // read valid slab bytes of another column (those D columns are unused).
+        // 16-bit reads: expert min(16 t + lane % 16, E - 1).
+        const bool tr = (E & 3) == 0;
+        uint32_t boff[C::ET];
+#pragma unroll
+        for (int b = 0; b < C::ET; ++b) {
+            const int t = C::kSplitE ? wave + 4 * b : b;
+            if (tr) {
+                const int e4 = min(16 * t + 4 * (lane & 3), E - 4);
+                boff[b] = (uint32_t)(((8 * g + ((lane & 15) >> 2)) * E + e4) * 2);
+            } else {
+                boff[b] = (uint32_t)((8 * g * E + min(16 * t + row, E - 1)) * 2);
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < C::NS - 1; ++st) issue(st);
+        for (int st = 0; st < nst; ++st) {
+            wait_vmcnt<(C::NS - 2) * C::ND>();
+            lds_barrier();
+            issue(st + C::NS - 1);
+            const uint32_t slot = ring0 + (uint32_t)((st % C::NS) * C::STAGE);
+            const uint32_t slab = slot + (uint32_t)(C::XU * 1024);
+#pragma unroll
+            for (int kq = 0; kq < C::KW; ++kq) {
+                const int kk = C::kSplitE ? kq : wave * C::KW + kq;   // k-step of the stage
+                const int c = 4 * kk + g;                             // chunk of the row
+                const uint32_t kbase = slab + (uint32_t)(kk * 32 * E * 2);
+                bf16x8_t bfr[C::ET];
+#pragma unroll
+                for (int b = 0; b < C::ET; ++b) {
+                    if (tr) {
+                        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_v4i16_t*)(uintptr_t)(kbase + boff[b]));
+                        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_v4i16_t*)(uintptr_t)(kbase + boff[b] + (uint32_t)(8 * E)));
+                        const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        bfr[b] = __builtin_bit_cast(bf16x8_t, v);
+                    } else {
+                        const lds_u16_t* pw =
+                            reinterpret_cast<const lds_u16_t*>((uintptr_t)(kbase + boff[b]));
+                        u32x4_t v;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            v[i] = (uint32_t)pw[(2 * i) * E] | ((uint32_t)pw[(2 * i + 1) * E] << 16);
+                        bfr[b] = __builtin_bit_cast(bf16x8_t, v);
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < C::TT; ++a) {
+                    const int r = 16 * a + row;
+                    const u32x4_t xa = *reinterpret_cast<const lds_u32x4_t*>(
+                        (uintptr_t)(slot + (uint32_t)(r * C::P + ((c ^ row_swz<C::CPR>(r)) << 4))));
+#pragma unroll
+                    for (int b = 0; b < C::ET; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xa), bfr[b], acc[a][b], 0, 0, 0);
+                }
+            }
+        }
+        wait_vmcnt<0>();
+        lds_barrier();
+        // D[token][expert]: lane holds tokens 16 a + 4 (lane / 16) + i of expert
+        // column 16 t + lane % 16
+        if constexpr (C::kSplitE) {
+#pragma unroll
+            for (int a = 0; a < C::TT; ++a)
+#pragma unroll
+                for (int b = 0; b < C::ET; ++b) {
+                    const int e = 16 * (wave + 4 * b) + row;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        lg[(16 * a + 4 * g + i) * C::E16 + e] = acc[a][b][i];
+                }
+        } else {
+#pragma unroll
+            for (int a = 0; a < C::TT; ++a)
+#pragma unroll
+                for (int b = 0; b < C::ET; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        red[(wave * C::TM + 16 * a + 4 * g + i) * C::E16 + 16 * b + row] =
+                            acc[a][b][i];
+        }
+    }
+    __syncthreads();
+
+    if constexpr (EB == 1) {
+        // ---- one thread per (token r, expert e); 16 tokens
+        const int r = tid >> 4, e = tid & 15, grp = lane & ~15, wv = tid >> 6;
+        const bool ev = e < E, tv = r < ntok;
+        float l;
+        if (!logits_in) {
+            l = ((red[(0 * 16 + r) * 16 + e] + red[(1 * 16 + r) * 16 + e]) +
+                 red[(2 * 16 + r) * 16 + e]) + red[(3 * 16 + r) * 16 + e];
+            if (ev && bg) l += __uint_as_float((uint32_t)bg[e] << 16);
+            if (ev && tv && logits_io) logits_io[(t0 + r) * E + e] = l;
+        } else {
+            l = (ev && tv) ? logits_io[(t0 + r) * E + e] : 0.f;
+        }
+        float m = ev ? l : -INFINITY;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+        const float pu = ev ? expf(l - m) : 0.f;                // unnormalised probability
+        float Z = pu;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) Z += __shfl_xor(Z, d);
+        int rank = 0;
+        for (int j = 0; j < E; ++j) {
+            const float lj = __shfl(l, grp | j);
+            rank += (lj > l) || (lj == l && j < e);
+        }
+        const bool sel = ev && rank < k;
+        // renormalised top-k weight: exp(l_e - m) / sum over the selected of exp(l - m)
+        float S = sel ? pu : 0.f;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) S += __shfl_xor(S, d);
+        if (sel && tv) {
+            o.topk_idx[(t0 + r) * k + rank] = e;
+            o.topk_w[(t0 + r) * k + rank] = pu / S;
+        }
+        // block partials: the 4 tokens of a wave by butterflies, then the
+        // waves in order
+        float ps = (ev && tv) ? pu / Z : 0.f;
+        int cnt = (sel && tv) ? 1 : 0;
+        float l2 = 0.f;
+        if (e == 0 && tv) {
+            const float lse = m + logf(Z);
+            l2 = lse * lse;
+        }
+#pragma unroll
+        for (int d = 16; d < 64; d <<= 1) {
+            ps += __shfl_xor(ps, d);
+            cnt += __shfl_xor(cnt, d);
+            l2 += __shfl_xor(l2, d);
+        }
+        __syncthreads();                         // every lane has read red
+        float* part = red;                       // [4 waves][16] probability sums
+        int* part_c = reinterpret_cast<int*>(red + 4 * 16);
+        float* part_l = red + 8 * 16;            // [4 waves]
+        if (lane < 16) {
+            part[wv * 16 + lane] = ps;
+            part_c[wv * 16 + lane] = cnt;
+            if (lane == 0) part_l[wv] = l2;
+        }
+        __syncthreads();
+        const int64_t blk = blockIdx.x, nblk = gridDim.x;
+        if (tid < E) {
+            o.blk_psum[tid * nblk + blk] =
+                ((part[tid] + part[16 + tid]) + part[32 + tid]) + part[48 + tid];
+            o.blk_cnt[tid * nblk + blk] =
+                part_c[tid] + part_c[16 + tid] + part_c[32 + tid] + part_c[48 + tid];
+        }
+        if (tid == 0) o.blk_lse2[blk] = ((part_l[0] + part_l[1]) + part_l[2]) + part_l[3];
+    } else {
+        // ---- logits tile [TM][E16]: the split-K sum, bias, optional output
+        for (int j = tid; j < C::TM * C::E16; j += kThreads) {
+            const int r = j / C::E16, e = j % C::E16;
+            float v = 0.f;
+            if (!logits_in) {
+                if constexpr (!C::kSplitE)
+                    v = ((red[j] + red[C::TM * C::E16 + j]) + red[2 * C::TM * C::E16 + j]) +
+                        red[3 * C::TM * C::E16 + j];
+                else
+                    v = lg[j];
+                if (e < E && bg) v += __uint_as_float((uint32_t)bg[e] << 16);
+                if (e < E && r < ntok && logits_io) logits_io[(t0 + r) * E + e] = v;
+            } else if (e < E && r < ntok) {
+                v = logits_io[(t0 + r) * E + e];
+            }
+            flag[j] = 0;
+            lg[j] = v;        // the split-K layout reads red[j] only for this j
+        }
+        __syncthreads();
+        // ---- LPT lanes per token
+        constexpr int LPT = C::LPT;
+        const int r = tid / LPT, q = tid % LPT;
+        const bool valid = r < ntok;
+        float* lr = lg + r * C::E16;
+        float m = -INFINITY;
+        for (int e = q; e < E; e += LPT) m = fmaxf(m, lr[e]);
+#pragma unroll
+        for (int d = 1; d < LPT; d <<= 1) m = fmaxf(m, __shfl_xor(m, d));
+        float Z = 0.f;
+        for (int e = q; e < E; e += LPT) Z += expf(lr[e] - m);
+#pragma unroll
+        for (int d = 1; d < LPT; d <<= 1) Z += __shfl_xor(Z, d);
+        uint64_t taken = 0;                 // bit j <=> expert q + LPT j taken
+        int sel[kMaxK];
+        float pv[kMaxK];
+        for (int s = 0; s < k; ++s) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            int j = 0;
+            for (int e = q; e < E; e += LPT, ++j) {
+                if ((taken >> j) & 1ull) continue;
+                const float v = lr[e];
+                if (bi == 0x7fffffff || v > bv) { bv = v; bi = e; }
+            }
+#pragma unroll
+            for (int d = 1; d < LPT; d <<= 1) {
+                const float ov = __shfl_xor(bv, d);
+                const int oi = __shfl_xor(bi, d);
+                if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            sel[s] = bi;
+            pv[s] = expf(bv - m) / Z;
+            if (bi % LPT == q) taken |= 1ull << (bi / LPT);
+        }
+        // every lane of the group holds the same sel / pv; lane 0 writes them
+        if (q == 0) {
+            float S = 0.f;
+            for (int s = 0; s < k; ++s) S += pv[s];
+            for (int s = 0; s < k; ++s) {
+                if (valid) {
+                    flag[r * C::E16 + sel[s]] = 1;
+                    o.topk_idx[(t0 + r) * k + s] = sel[s];
+                    o.topk_w[(t0 + r) * k + s] = pv[s] / S;
+                }
+            }
+            const float lse = m + logf(Z);
+            lse_s[r] = valid ? lse * lse : 0.f;
+        }
+        // probabilities of all experts (for the load-balancing loss)
+        for (int e = q; e < E; e += LPT) lr[e] = valid ? expf(lr[e] - m) / Z : 0.f;
+        __syncthreads();
+        // ---- per 16-token block partials, tokens in order (independent loads)
+        const int64_t nblk = (T + kRouteTok - 1) / kRouteTok;
+        constexpr int NB = C::TM / kRouteTok;
+        for (int j = tid; j < NB * E; j += kThreads) {
+            const int b = j / E, e = j % E;
+            const int64_t blk = t0 / kRouteTok + b;
+            if (blk >= nblk) continue;
+            float pr[kRouteTok];
+            int fl[kRouteTok];
+#pragma unroll
+            for (int rr = 0; rr < kRouteTok; ++rr) {
+                pr[rr] = lg[(b * kRouteTok + rr) * C::E16 + e];
+                fl[rr] = flag[(b * kRouteTok + rr) * C::E16 + e];
+            }
+            float ps = 0.f;
+            int c = 0;
+#pragma unroll
+            for (int rr = 0; rr < kRouteTok; ++rr) {
+                ps += pr[rr];
+                c += fl[rr];
+            }
+            o.blk_psum[e * nblk + blk] = ps;            // column-major: [E][nblk]
+            o.blk_cnt[e * nblk + blk] = c;
+        }
+        if (tid < NB) {
+            const int64_t blk = t0 / kRouteTok + tid;
+            if (blk < nblk) {
+                float a = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < kRouteTok; ++rr) a += lse_s[tid * kRouteTok + rr];
+                o.blk_lse2[blk] = a;
+            }
+        }
+    }
+}
+
+template <int EB>
+static void launch_route_bf16(hipStream_t s, const uint16_t* x, const uint16_t* Wg,
+                              const uint16_t* bg, float* logits, int logits_in, int64_t T, int H,
+                              int E, int k, RouteOut o) {
+    const int64_t nwg = (T + RouteCfg<EB>::TM - 1) / RouteCfg<EB>::TM;
+    route_bf16<EB><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(x, Wg, bg, logits, logits_in,
+                                                                    T, H, E, k, o);
 }
 
 // ---------------------------------------------------------------- fp32 router
@@ -477,13 +554,13 @@ __global__ __launch_bounds__(kThreads) void route_f32(
 }
 
 // ---------------------------------------------------------------- finalize
-// E + 1 column workgroups, then one thread for the losses.
+// E + 1 column workgroups, then one wave for the losses.
 __global__ __launch_bounds__(kColThreads) void route_fin_columns(FinArgs f, int E) {
     fin_column_block(f, E, blockIdx.x);
 }
 
-__global__ void route_fin_losses(FinArgs f, int E) {
-    if (threadIdx.x == 0) fin_losses(f, E);
+__global__ __launch_bounds__(64) void route_fin_losses(FinArgs f, int E) {
+    fin_losses(f, E);
 }
 
 }  // namespace
@@ -505,31 +582,12 @@ hipError_t launch_route(const moe_problem_t& p, const WsLayout& L, char* ws, con
         auto* xb = static_cast<const uint16_t*>(x);
         auto* wb = static_cast<const uint16_t*>(Wg);
         auto* bb = static_cast<const uint16_t*>(bg);
-        if (!logits_in && E <= 16) {
-            if (E <= 8)
-                route_bf16_ring<8><<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(
-                    xb, wb, bb, logits, T, H, E, k, o);
-            else
-                route_bf16_ring<16><<<dim3((unsigned)nblk), dim3(kThreads), 0, s>>>(
-                    xb, wb, bb, logits, T, H, E, k, o);
-        } else {
-            uint16_t* WgT = reinterpret_cast<uint16_t*>(ws + L.wgt);
-            if (!logits_in) {
-                const int64_t n = (int64_t)H * E;
-                gate_transpose_bf16<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
-                    wb, WgT, H, E);
-            }
-            const int NT = (E + 15) / 16;
-            const int NTp = NT <= 1 ? 1 : NT <= 2 ? 2 : NT <= 4 ? 4 : NT <= 8 ? 8 : 16;
-            const int li = logits_in ? 1 : 0;
-            switch (NTp) {
-                case 1: launch_route_bf16_nt<1>(nblk, s, xb, WgT, bb, logits, li, T, H, E, k, o); break;
-                case 2: launch_route_bf16_nt<2>(nblk, s, xb, WgT, bb, logits, li, T, H, E, k, o); break;
-                case 4: launch_route_bf16_nt<4>(nblk, s, xb, WgT, bb, logits, li, T, H, E, k, o); break;
-                case 8: launch_route_bf16_nt<8>(nblk, s, xb, WgT, bb, logits, li, T, H, E, k, o); break;
-                default: launch_route_bf16_nt<16>(nblk, s, xb, WgT, bb, logits, li, T, H, E, k, o); break;
-            }
-        }
+        const int li = logits_in ? 1 : 0;
+        if (E <= 16) launch_route_bf16<1>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 32) launch_route_bf16<2>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 64) launch_route_bf16<4>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 128) launch_route_bf16<8>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else launch_route_bf16<16>(s, xb, wb, bb, logits, li, T, H, E, k, o);
     } else {
         const size_t lds = sizeof(float) * (size_t)kRouteTok * E;
         route_f32<<<dim3((unsigned)nblk), dim3(kThreads), lds, s>>>(
