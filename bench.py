@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd tokens/s and FFN TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PMC_FILE = os.path.join(ROOT, "profiles", "ffn_gemm_traffic_mixtral_T16384_H4096_E8_k2_F14336.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -51,14 +51,16 @@ def parse():
     ap.add_argument("--no-abi-timing", action="store_true",
                     help="skip the per-call warm/cold timing that follows the timed steps "
                          "(thousands of extra launches; counter runs of the profiler omit it)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU work for the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=90.0,
+                    help="the oracle runs the whole forward when a probe predicts at most this "
+                         "many seconds, else a token prefix of about this much work")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device-to-device copy of MIB MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
-                         "WRITE_SIZE, both with --calibrate-copy) into profiles/pmc_traffic.json")
+                         "WRITE_SIZE, both with --calibrate-copy) into "
+                         "profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -66,45 +68,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the sources that define the expert GEMM kernels the traffic counters describe
-GEMM_SOURCES = ("expert_gemm.hip", "gemm_common.h", "lds_dma.h", "moe_internal.h")
-
-
 def kernel_source_hash() -> str:
+    """Hash of every kernel and host source of the library: traffic figures taken
+    on other sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mixture_experts_21_amd", "csrc")
-    for f in GEMM_SOURCES:
+    for f in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel sources and the same workload."""
+    was taken on the current sources and the same workload."""
     try:
-        with open(PMC_FILE) as fh:
+        with open(traffic_path(workload)) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != kernel_source_hash():
-        return None
-    if d.get("workload") != workload:
+    if d.get("source_hash") != kernel_source_hash() or d.get("workload") != workload:
         return None
     k = d.get("kernels", {}).get(kernel)
     return None if not k else k.get("hbm_bytes")
 
 
+def kernel_key(symbol: str) -> str:
+    """Short name of a kernel symbol: the expert GEMM as up / down (template
+    arguments <BM, activation, save>: activation 0 is the second GEMM), else
+    the function name."""
+    base = symbol.split("(")[0]
+    name = base.split("<")[0].split("::")[-1].strip()
+    if name == "ffn_gemm_bf16":
+        targs = [a.strip() for a in base.split("<", 1)[1].split(">")[0].split(",")]
+        return "ffn_gemm_bf16_down" if targs[1] == "0" else "ffn_gemm_bf16_up"
+    return name
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int = 256):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the expert GEMMs, scaled by
-    what the same counters read for the calibration copy of known size."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel of the run,
+    scaled by what the same counters read for the calibration copy of known
+    size, in bytes per launch."""
     import csv
     import glob
 
     def per_kernel(d, counter):
-        # mean per dispatch, keyed by (kernel, grid size); the calibration copy
-        # is the copy dispatch with the largest grid
+        # mean per dispatch, keyed by kernel; the calibration copy is the copy
+        # dispatch with the largest grid
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
@@ -116,37 +131,36 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int =
                 if g > copy[0]:
                     copy = (g, v)
                 continue
-            acc.setdefault(r["Kernel_Name"], []).append(v)
+            if "fill" in r["Kernel_Name"] or "elementwise" in r["Kernel_Name"]:
+                continue
+            acc.setdefault(kernel_key(r["Kernel_Name"]), []).append(v)
         return {k: sum(v) / len(v) for k, v in acc.items()}, copy[1]
 
     (fetch, c_fetch), (write, c_write) = (per_kernel(fetch_dir, "FETCH_SIZE"),
                                           per_kernel(write_dir, "WRITE_SIZE"))
     if c_fetch is None or c_write is None:
         raise SystemExit("no calibration copy kernel found in the pmc runs")
-    ck = "__amd_rocclr_copyBuffer"
     kib = copy_mib * 1024.0
     f_fetch, f_write = c_fetch / kib, c_write / kib
-    out = {"source_hash": kernel_source_hash(), "workload": workload, "calibration_kernel": ck,
-           "calibration_copy_kib": kib, "fetch_factor": f_fetch, "write_factor": f_write,
-           "kernels": {}}
-    lines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |", "|---|---|---|---|"]
-    for k in sorted(fetch):
-        if "ffn_gemm_bf16" not in k:
-            continue
-        # template arguments <BM, activation, save>: activation 0 is the second GEMM
-        targs = [a.strip() for a in k.split("<", 1)[1].split(">")[0].split(",")]
-        name = "ffn_gemm_bf16_down" if targs[1] == "0" else "ffn_gemm_bf16_up"
+    out = {"source_hash": kernel_source_hash(), "workload": workload,
+           "calibration_kernel": "__amd_rocclr_copyBuffer", "calibration_copy_kib": kib,
+           "fetch_factor": f_fetch, "write_factor": f_write, "kernels": {}}
+    lines = ["| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (scaled) |",
+             "|---|---|---|---|"]
+    for k in sorted(fetch, key=lambda n: -fetch[n]):
         hbm = (fetch[k] / f_fetch + write.get(k, 0.0) / f_write) * 1024.0
-        out["kernels"][name] = {"symbol": k, "fetch_kib": fetch[k], "write_kib": write.get(k),
-                                "hbm_bytes": hbm}
-        lines.append(f"| {name} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {hbm:.4g} |")
+        out["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write.get(k), "hbm_bytes": hbm}
+        lines.append(f"| {k} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {hbm:.4g} |")
     return out, lines
 
 
-def cpu_baseline(spec, inp, target_s: float):
-    """Time the fp64 oracle on the host: routing + dispatch over all T tokens,
-    the expert FFN + combine on a contiguous token prefix sized to ~target_s of
-    work, scaled linearly to T (the FFN is per token)."""
+def cpu_baseline(spec, inp, limit_s: float):
+    """Time the fp64 oracle on the host: the whole forward (gate, softmax, top-k,
+    losses, dispatch, expert FFN, combine) over all T tokens when a probe
+    predicts it fits in limit_s seconds; otherwise routing and dispatch over
+    all T tokens plus the expert FFN and combine on a contiguous token prefix
+    sized to limit_s, scaled linearly to T (the FFN is per token), and the
+    sample says so."""
     import numpy as np
     import oracle as om
     t0 = time.perf_counter()
@@ -173,11 +187,14 @@ def cpu_baseline(spec, inp, target_s: float):
     threads = om.num_threads()
     n0 = min(spec.T, max(threads, 8))
     t_probe = ffn(n0)
-    n = int(min(spec.T, max(n0, n0 * max(target_s - t_route, 1.0) / max(t_probe, 1e-6))))
+    est = t_probe * spec.T / n0
+    if est <= limit_s:
+        n = spec.T
+    else:
+        n = int(min(spec.T, max(n0, n0 * max(limit_s - t_route, 1.0) / max(t_probe, 1e-6))))
     t_ffn = ffn(n) if n > n0 else t_probe
-    per_tok = t_ffn / n
-    total = t_route + per_tok * spec.T
-    kept = int(kept_mask[:n].sum())                          # kept pairs of the sample
+    total = t_route + t_ffn * spec.T / n
+    kept = int(kept_mask[:n].sum())                          # kept pairs of the timed tokens
     flops = 2.0 * spec.T * spec.H * spec.E + 4.0 * spec.H * spec.F * kept
     cpu = "unknown"
     try:
@@ -188,13 +205,32 @@ def cpu_baseline(spec, inp, target_s: float):
                     break
     except OSError:
         pass
+    route_what = ("gate/softmax/expert choice" if spec.ec_group
+                  else "gate/softmax/top-k/losses/dispatch")
+    if n == spec.T:
+        sample = (f"fp64 C oracle, {threads} OpenMP threads: the whole forward of all "
+                  f"{spec.T} tokens ({route_what} {t_route:.2f} s, expert FFN and combine "
+                  f"{t_ffn:.2f} s), no scaling")
+    else:
+        sample = (f"fp64 C oracle, {threads} OpenMP threads: {route_what} over all {spec.T} "
+                  f"tokens ({t_route:.2f} s) + expert FFN and combine on tokens 0..{n - 1} "
+                  f"({t_ffn:.2f} s), FFN time scaled linearly to {spec.T} tokens "
+                  f"(the whole forward was estimated at {est:.0f} s)")
     return {"value": spec.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu": cpu, "gflops": flops / (t_route + t_ffn) / 1e9,
-            "sample": (f"fp64 C oracle, {threads} OpenMP threads: "
-                       f"{'gate/softmax/expert choice' if spec.ec_group else 'gate/softmax/top-k/losses/dispatch'}"
-                       f" over all {spec.T} tokens ({t_route:.2f} s) + expert FFN and "
-                       f"combine on tokens 0..{n - 1} ({t_ffn:.2f} s), FFN time scaled "
-                       f"linearly to {spec.T} tokens")}
+            "cpu": cpu, "gflops": flops / (t_route + t_ffn) / 1e9, "seconds": t_route + t_ffn,
+            "scaled": n != spec.T, "sample": sample}
+
+
+def routing_stats(E, counts, offsets, cap, T, k):
+    """Per-expert load before and after capacity, and what capacity dropped."""
+    import numpy as np
+    counts = np.asarray(counts, np.int64)
+    kept = np.diff(np.asarray(offsets, np.int64))
+    return {"load_max": int(counts.max()), "load_min": int(counts.min()),
+            "kept_max": int(kept.max()), "kept_min": int(kept.min()),
+            "experts_empty": int((counts == 0).sum()), "capacity": int(cap),
+            "dropped_pairs": int(T * k - kept.sum()),
+            "drop_fraction": float((T * k - kept.sum()) / (T * k))}
 
 
 def _token_choice_calls(moe, prob, d, ws, out, losses, idx, tw, counts, offsets, pos, row_token,
@@ -410,7 +446,7 @@ def main():
         import workloads as W
         out, lines = summarize_pmc(*args.summarize_pmc, W.CONFIGS[args.config].name,
                                    args.calibrate_copy or 256)
-        with open(PMC_FILE, "w") as fh:
+        with open(traffic_path(W.CONFIGS[args.config].name), "w") as fh:
             json.dump(out, fh, indent=1)
         print("\n".join(lines))
         print(f"fetch factor {out['fetch_factor']:.4f}, write factor {out['write_factor']:.4f} "
@@ -459,15 +495,17 @@ def main():
     out = torch.empty(T, H, dtype=sd, device="cuda")
     losses = torch.empty(2, dtype=torch.float32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    rowof = torch.empty(T, E, dtype=torch.int32, device="cuda") if g else None
     evs = [moe.StageEvents() for _ in range(args.steps)]
 
     def step(ev=None):
         if g:       # expert choice: every expert takes C tokens of each group
             moe.moe_forward_expert_choice(prob, g, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"],
-                                          d["W2"], d["b2"], out, ws, events=ev)
+                                          d["W2"], d["b2"], out, ws, rowof=rowof, events=ev)
         else:
             moe.moe_forward(prob, d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"],
-                            out, losses, ws, offsets=offsets, events=ev)
+                            out, losses, ws, counts=counts, offsets=offsets, events=ev)
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -607,6 +645,11 @@ def main():
                        / (abi["combine"]["cold"]["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
         "losses": None if g else [float(v) for v in losses.cpu().numpy()],
+        "routing_stats": routing_stats(E, counts.cpu().numpy(), offsets.cpu().numpy(),
+                                 moe.moe_capacity(prob), T, k) if not g else {
+            "rows_per_expert": A // E, "capacity_per_group": moe.moe_ec_capacity(prob, g),
+            "tokens_taken_by_no_expert": int(((rowof >= 0).sum(dim=1) == 0).sum().item()),
+            "tokens_taken_by_3_or_more": int(((rowof >= 0).sum(dim=1) >= 3).sum().item())},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
