@@ -4,6 +4,8 @@
 // row).  Token-major gather instead of a scatter-add: every output element is
 // produced by exactly one thread, summed in fp32 in slot order and rounded
 // once, so there are no atomics and results are bitwise reproducible.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,23 +26,27 @@ __device__ __forceinline__ void st_stream(V* p, V v) {
     else *p = v;
 }
 
-// One workgroup = one token row; a thread owns kCombVec 16-byte vectors
-// (8 bf16 or 4 fp32 each) per pass.  The token's (row, weight) pairs are
-// workgroup-uniform and taken kMaxK slots at a time (one chunk for top-k
-// routing; expert choice passes one slot per expert); every kept slot's
-// vectors of a chunk are loaded before they are added, in fp32 and in slot
-// order, and the sum is rounded once.
+// TPT threads (1 to 4 waves) per token row, sized to the row so that a row
+// of up to TPT * kCombVec 16-byte vectors (8 bf16 or 4 fp32 each) goes in one
+// pass and narrow rows do not leave most of a workgroup idle; a workgroup
+// holds 256 / TPT tokens.  The token's (row, weight) pairs are uniform over
+// its threads and taken kMaxK slots at a time (one chunk for top-k routing;
+// expert choice passes one slot per expert); every kept slot's vectors of a
+// chunk are loaded before they are added, in fp32 and in slot order, and the
+// sum is rounded once.
 constexpr int kCombThreads = 256;
 constexpr int kCombVec = 2;
 
-template <bool BF16>
+template <bool BF16, int TPT>
 __global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __restrict__ y,
                                                              const int32_t* __restrict__ pos,
                                                              const float* __restrict__ topk_w,
-                                                             int k, int64_t vec,
+                                                             int k, int64_t T, int64_t vec,
                                                              u32x4_t* __restrict__ out) {
-    const int64_t t = blockIdx.x;
-    for (int64_t v0 = threadIdx.x; v0 < vec; v0 += kCombThreads * kCombVec) {
+    const int lane = threadIdx.x % TPT;
+    const int64_t t = (int64_t)blockIdx.x * (kCombThreads / TPT) + threadIdx.x / TPT;
+    if (t >= T) return;                                   // whole waves
+    for (int64_t v0 = lane; v0 < vec; v0 += TPT * kCombVec) {
         float acc[kCombVec][8];
 #pragma unroll
         for (int u = 0; u < kCombVec; ++u)
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __re
                 if (row[s] < 0) continue;              // uniform: no divergence
 #pragma unroll
                 for (int u = 0; u < kCombVec; ++u) {
-                    const int64_t v = v0 + (int64_t)u * kCombThreads;
+                    const int64_t v = v0 + (int64_t)u * TPT;
                     if (v < vec) d[s][u] = ld_stream(&y[(int64_t)row[s] * vec + v]);
                 }
             }
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __re
         }
 #pragma unroll
         for (int u = 0; u < kCombVec; ++u) {
-            const int64_t v = v0 + (int64_t)u * kCombThreads;
+            const int64_t v = v0 + (int64_t)u * TPT;
             if (v >= vec) continue;
             u32x4_t o;
             if (BF16) {
@@ -100,20 +106,31 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows(const u32x4_t* __re
     }
 }
 
+template <bool BF16>
+hipError_t launch_rows(const moe_problem_t& p, const void* y, const int32_t* pos,
+                       const float* topk_w, void* out, int64_t vec, hipStream_t s) {
+    auto* yv = static_cast<const u32x4_t*>(y);
+    auto* ov = static_cast<u32x4_t*>(out);
+    auto go = [&](auto tpt) {
+        constexpr int TPT = decltype(tpt)::value;
+        const unsigned nb = (unsigned)((p.T + (kCombThreads / TPT) - 1) / (kCombThreads / TPT));
+        combine_rows<BF16, TPT><<<dim3(nb), dim3(kCombThreads), 0, s>>>(yv, pos, topk_w, p.k, p.T,
+                                                                         vec, ov);
+    };
+    if (vec > 128 * kCombVec) go(std::integral_constant<int, 256>{});
+    else if (vec > 64 * kCombVec) go(std::integral_constant<int, 128>{});
+    else go(std::integral_constant<int, 64>{});
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s) {
     const bool bf16 = p.dtype == MOE_DTYPE_BF16;
     const int64_t vec = (int64_t)p.H * (bf16 ? 2 : 4) / 16;
-    const unsigned nb = (unsigned)p.T;
-    if (bf16)
-        combine_rows<true><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
-            static_cast<const u32x4_t*>(y), pos, topk_w, p.k, vec, static_cast<u32x4_t*>(out));
-    else
-        combine_rows<false><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
-            static_cast<const u32x4_t*>(y), pos, topk_w, p.k, vec, static_cast<u32x4_t*>(out));
-    return hipGetLastError();
+    return bf16 ? launch_rows<true>(p, y, pos, topk_w, out, vec, s)
+                : launch_rows<false>(p, y, pos, topk_w, out, vec, s);
 }
 
 }  // namespace moe

@@ -142,17 +142,20 @@ __device__ void route_epilogue(float* logit_s, int32_t* idx_s, float* lse_s, int
 // softmax probabilities and the expert counts (tokens in a fixed order) and
 // the sum of lse^2, column-major [E][nblk], for the fixed-order loss
 // reduction.
-template <int EB>   // 16-expert tiles: E <= 16 EB
+// EB: 16-expert tiles (E <= 16 EB); TM tokens per workgroup; BK hidden units
+// per stage; NS stages; WE gate columns reserved per stage (E <= WE); SE:
+// waves own expert tiles (else they split the k-steps).
+template <int EB, int TM_, int BK_, int NS_, int WE, bool SE>
 struct RouteCfg {
-    static constexpr bool kSplitE = EB >= 8;              // waves own expert tiles
-    static constexpr int TM = EB == 1 ? 16 : 32;          // tokens per workgroup
-    static constexpr int BK = EB == 1 ? 256 : EB <= 8 ? 128 : 64;     // h per stage
-    static constexpr int NS = EB >= 8 ? 2 : 3;            // LDS stages
+    static constexpr bool kSplitE = SE;
+    static constexpr int TM = TM_;
+    static constexpr int BK = BK_;
+    static constexpr int NS = NS_;
     static constexpr int E16 = 16 * EB;
     static constexpr int P = BK * 2;                      // bytes of a token row per stage
     static constexpr int CPR = P / 16;                    // 16-byte chunks per row
     static constexpr int XU = TM * P / 1024;              // 1 KB DMAs for the token rows
-    static constexpr int WUMAX = (BK * E16 * 2 + 1023) / 1024;   // ... for the gate slab
+    static constexpr int WUMAX = (BK * WE * 2 + 1023) / 1024;    // ... for the gate slab
     static constexpr int ND = (XU + WUMAX + 3) / 4;       // DMAs per wave per stage
     static constexpr int STAGE = (XU + WUMAX) * 1024;
     static constexpr int KS = BK / 32;                    // k-steps per stage
@@ -160,6 +163,7 @@ struct RouteCfg {
     static constexpr int TT = TM / 16;                    // token tiles
     static constexpr int ET = kSplitE ? EB / 4 : EB;      // expert tiles per wave
     static constexpr int LPT = 256 / TM;                  // epilogue lanes per token
+    static constexpr bool kLane16 = EB == 1 && TM == 16;  // one lane per (token, expert)
     // epilogue LDS: split-K partial tiles [4][TM][E16] (or none), logits
     // [TM][E16], selection flags [TM][E16], lse^2 [TM]
     static constexpr int RED = kSplitE ? 0 : 4 * TM * E16 * 4;
@@ -167,8 +171,9 @@ struct RouteCfg {
     static constexpr int RING = NS * STAGE + 1024;        // + a sink for padding DMAs
     static constexpr int LDS = RING > EPI ? RING : EPI;
     static_assert(TM * P % 1024 == 0 && 1024 % P == 0, "whole rows per DMA");
-    static_assert(kSplitE ? EB % 4 == 0 : KS % 4 == 0, "work split");
-    static_assert(EB != 1 || TM == 16, "the 16-lane epilogue takes 16 tokens");
+    static_assert(kSplitE ? (EB % 4 == 0) : (KS % 4 == 0), "work split");
+    static_assert(TM == 16 || TM == 32 || TM == 64, "epilogue lane groups");
+    static_assert(WE >= 16 * EB - 15 && WE <= 16 * EB, "gate columns");
 };
 
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
@@ -185,12 +190,12 @@ __device__ __forceinline__ int row_swz(int r) {
     else return (r >> 2) & 3;
 }
 
-template <int EB>
+template <int EB, int TM_, int BK_, int NS_, int WE, bool SE>
 __global__ __launch_bounds__(kThreads) void route_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ bg, float* __restrict__ logits_io, int logits_in, int64_t T,
     int H, int E, int k, RouteOut o) {
-    using C = RouteCfg<EB>;
+    using C = RouteCfg<EB, TM_, BK_, NS_, WE, SE>;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void route_bf16(
     }
     __syncthreads();
 
-    if constexpr (EB == 1) {
+    if constexpr (C::kLane16) {
         // ---- one thread per (token r, expert e); 16 tokens
         const int r = tid >> 4, e = tid & 15, grp = lane & ~15, wv = tid >> 6;
         const bool ev = e < E, tv = r < ntok;
@@ -513,13 +518,13 @@ __global__ __launch_bounds__(kThreads) void route_bf16(
     }
 }
 
-template <int EB>
+template <int EB, int TM, int BK, int NS, int WE, bool SE>
 static void launch_route_bf16(hipStream_t s, const uint16_t* x, const uint16_t* Wg,
                               const uint16_t* bg, float* logits, int logits_in, int64_t T, int H,
                               int E, int k, RouteOut o) {
-    const int64_t nwg = (T + RouteCfg<EB>::TM - 1) / RouteCfg<EB>::TM;
-    route_bf16<EB><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(x, Wg, bg, logits, logits_in,
-                                                                    T, H, E, k, o);
+    const int64_t nwg = (T + TM - 1) / TM;
+    route_bf16<EB, TM, BK, NS, WE, SE><<<dim3((unsigned)nwg), dim3(kThreads), 0, s>>>(
+        x, Wg, bg, logits, logits_in, T, H, E, k, o);
 }
 
 // ---------------------------------------------------------------- fp32 router
@@ -583,11 +588,22 @@ hipError_t launch_route(const moe_problem_t& p, const WsLayout& L, char* ws, con
         auto* wb = static_cast<const uint16_t*>(Wg);
         auto* bb = static_cast<const uint16_t*>(bg);
         const int li = logits_in ? 1 : 0;
-        if (E <= 16) launch_route_bf16<1>(s, xb, wb, bb, logits, li, T, H, E, k, o);
-        else if (E <= 32) launch_route_bf16<2>(s, xb, wb, bb, logits, li, T, H, E, k, o);
-        else if (E <= 64) launch_route_bf16<4>(s, xb, wb, bb, logits, li, T, H, E, k, o);
-        else if (E <= 128) launch_route_bf16<8>(s, xb, wb, bb, logits, li, T, H, E, k, o);
-        else launch_route_bf16<16>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        // shapes per gate width, from a sweep on one MI355X: with E <= 8 the
+        // 37 KB ring lets 4 workgroups share a CU, so the Mixtral-shaped batch
+        // (1024 workgroups) runs in one round; wide gates are bound by
+        // re-streaming the whole gate through every workgroup
+        if (E <= 8)
+            launch_route_bf16<1, 16, 256, 3, 8, false>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 16)
+            launch_route_bf16<1, 16, 256, 3, 16, false>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 32)
+            launch_route_bf16<2, 32, 128, 3, 32, false>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 64)
+            launch_route_bf16<4, 32, 64, 4, 64, true>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else if (E <= 128)
+            launch_route_bf16<8, 16, 64, 2, 128, true>(s, xb, wb, bb, logits, li, T, H, E, k, o);
+        else
+            launch_route_bf16<16, 32, 64, 2, 256, true>(s, xb, wb, bb, logits, li, T, H, E, k, o);
     } else {
         const size_t lds = sizeof(float) * (size_t)kRouteTok * E;
         route_f32<<<dim3((unsigned)nblk), dim3(kThreads), lds, s>>>(
