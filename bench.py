@@ -102,7 +102,7 @@ def kernel_key(symbol: str) -> str:
     """Short name of a kernel symbol: the expert GEMM as up / down (template
     arguments <BM, activation, save>: activation 0 is the second GEMM), else
     the function name."""
-    base = symbol.split("(")[0]
+    base = symbol.replace("(anonymous namespace)::", "").split("(")[0]
     name = base.split("<")[0].split("::")[-1].strip()
     if name == "ffn_gemm_bf16":
         targs = [a.strip() for a in base.split("<", 1)[1].split(">")[0].split(",")]
@@ -607,6 +607,14 @@ def main():
         }
     hbm = {n: {"ms": sm[n], "GB/s": alg_bytes[n] / (sm[n] * 1e-3) / 1e9,
                "frac": alg_bytes[n] / (sm[n] * 1e-3) / 1e9 / PEAK_HBM_GBS} for n in alg_bytes}
+    # calibrated FETCH + WRITE bytes of the stage's kernels from profiles/, when
+    # they were taken on these sources and this workload
+    stage_kernels = {"route": ("route_bf16",), "permute": ("scan_columns", "chunk_rank"),
+                     "combine": ("combine_rows",)}
+    for n, ks in stage_kernels.items():
+        tr = [traffic_for(kk, spec.name) for kk in ks]
+        if n in hbm:
+            hbm[n]["traffic"] = None if g or any(v is None for v in tr) else sum(tr)
     kern = "ffn_gemm_bf16_up" if dom == "ffn_up" else "ffn_gemm_bf16_down"
     res = {
         "metric": METRIC,
