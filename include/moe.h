@@ -189,7 +189,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg,
  * process ends (its device address is looked up on the first call on that
  * device).  Problems whose moe_workspace_bytes() exceeds it return
  * MOE_ERR_WORKSPACE before anything is enqueued (64 MiB holds the
- * Mixtral-shaped layer up to 448 tokens).  No call allocates or frees
+ * Mixtral-shaped layer up to 454 tokens).  No call allocates or frees
  * anything.  Every call on one GPU uses the same array: calls that overlap on
  * one GPU (two streams, two threads) race and give undefined results;
  * serialise them.  Nothing needs clearing between calls: each forward writes

@@ -752,21 +752,6 @@ int pick_bm(const moe_problem_t& p) {
     return 256;
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cus[64] = {0};
-    int d = 0;
-    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
-    if (cus[d] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cus[d] = n;
-    }
-    return cus[d];
-}
-
 int gemm_nt(int N) { return (N + 255) / 256; }
 
 // Every real tile, plus room for one round of K slices; the fixup covers at

@@ -2,6 +2,7 @@
 // launch sequence of every stage.  All validation happens before the first
 // HIP call, so a rejected call enqueues nothing (and needs no GPU).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -12,6 +13,20 @@
 namespace moe {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return 256;
+    int n = cus[d].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[d].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 WsLayout ws_layout(const moe_problem_t& p) {
     WsLayout L;
@@ -28,12 +43,12 @@ WsLayout ws_layout(const moe_problem_t& p) {
         return o;
     };
     const size_t nb = (size_t)L.nblk_route, nc = (size_t)L.nchunk;
-    L.wgt = take(p.dtype == MOE_DTYPE_BF16 ? E * H * 2 : 0);
     L.blk_psum = take(nb * E * 4);
     L.blk_lse2 = take(nb * 4);
     L.blk_cnt = take(nb * E * 4);
     L.fin_sum = take((E + 1) * 8);
     L.fin_cnt = take(E * 8);
+    L.small_disp = take(route_small_fits(p) ? (E + 1 + 2 * T * k) * 4 : 0);
     L.route_bytes = off;
     L.chunk_hist = take(nc * E * 4);
     L.chunk_base = take(nc * E * 4);
@@ -356,8 +371,18 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* Wg, co
         return MOE_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(*p);
     if (ws_bytes < L.route_bytes) return MOE_ERR_WORKSPACE;
-    hipError_t e = launch_route(*p, L, static_cast<char*>(ws), x, Wg, bg, logits, logits_in,
-                                topk_idx, topk_w, counts, losses, true, stream);
+    hipError_t e;
+    if (!logits_in && route_small_fits(*p)) {
+        // the launch moe_forward takes for a few tokens, so that the stages
+        // reproduce its routing bit for bit; its dispatch outputs are dropped
+        int32_t* sd = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.small_disp);
+        const int64_t pairs = p->T * p->k;
+        e = launch_route_small(*p, capacity_of(*p), x, Wg, bg, logits, topk_idx, topk_w, counts,
+                               losses, sd, sd + p->E + 1, sd + p->E + 1 + pairs, stream);
+    } else {
+        e = launch_route(*p, L, static_cast<char*>(ws), x, Wg, bg, logits, logits_in, topk_idx,
+                         topk_w, counts, losses, true, stream);
+    }
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

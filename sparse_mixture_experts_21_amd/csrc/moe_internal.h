@@ -37,12 +37,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // regions are 256-byte aligned.  Regions a call does not use are still laid
 // out so that one layout serves every entry point.
 struct WsLayout {
-    size_t wgt;          // gate weights transposed to [E][H] (bf16 router, E > 16)
     size_t blk_psum;     // [E][nblk_route] fp32: per-block sums of softmax probs
     size_t blk_lse2;     // [nblk_route]    fp32: per-block sums of lse^2
     size_t blk_cnt;      // [E][nblk_route] int32: per-block expert histograms
     size_t fin_sum;      // [E + 1] fp64: column sums of the router partials
     size_t fin_cnt;      // [E] int64: expert counts from the router partials
+    size_t small_disp;   // [E + 1 + 2 T k] int32: offsets, pos, row_token that moe_route
+                         // drops when a few tokens route in one launch (route_small)
     size_t chunk_hist;   // [E][nchunk] int32 expert histogram per chunk
     size_t chunk_base;   // [E][nchunk] int32 pairs routed to e before the chunk
     size_t col_tot;      // [E] int32: pairs routed to each expert
@@ -59,6 +60,8 @@ constexpr int kChunkTok = 16;      // tokens per dispatch chunk: one router bloc
 static_assert(kChunkTok == kRouteTok, "dispatch chunks are router blocks");
 
 WsLayout ws_layout(const moe_problem_t& p);
+// Compute units of the current device (looked up once per device).
+int device_cus();
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.

@@ -51,6 +51,8 @@ SMALL = [
     S("ec_bf16_T32768_H64_E4_k1_F128_seq32768", 32768, 64, 4, 1, 128, 32768),
     # all logits tie: every expert takes the first C tokens of each group
     W.zero_gate(S("ec_zero_gate_T600_H128_E8_k2_F256_seq200", 600, 128, 8, 2, 256, 200)),
+    # a decode-sized batch: two 3-token groups
+    S("ec_bf16_T6_H264_E4_k2_F776_seq3", 6, 264, 4, 2, 776, 3),
 ]
 
 

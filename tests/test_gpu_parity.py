@@ -83,14 +83,26 @@ TINY = [
     W.zero_gate(S("tiny_zero_gate_T3_H128_E8_k2_F64_cf0.5", 3, 128, 8, 2, 64, cf=0.5)),
     S("tiny_silu_T2_H512_E8_k2_F256", 2, 512, 8, 2, 256, act="silu"),
 ]
+# Decode-sized batches (T <= 8): every GEMM tile holds a few real rows and is
+# cut along K.  A ragged K and N (partial k-tile and column tile), more than
+# 64 experts with a few active, every expert holding every token, one expert,
+# and a long K (down GEMM with F = 8200).
+FEW = [
+    S("few_T1_H512_E8_k2_F2048", 1, 512, 8, 2, 2048, biases=True),
+    S("few_T3_H264_E6_k2_F776", 3, 264, 6, 2, 776, biases=True),
+    S("few_T8_H256_E128_k8_F512_cf0.5", 8, 256, 128, 8, 512, cf=0.5, wg=W.Dist("normal", 0.1)),
+    S("few_silu_T7_H1032_E4_k4_F136", 7, 1032, 4, 4, 136, act="silu"),
+    S("few_T2_H128_E1_k1_F64", 2, 128, 1, 1, 64, biases=True),
+    S("few_T8_H128_E2_k1_F8200", 8, 128, 2, 1, 8200, biases=True),
+]
 
 
 def _small_ids():
-    return [s.name for s in SMALL + TINY]
+    return [s.name for s in SMALL + TINY + FEW]
 
 
 # ---------------------------------------------------------------- end to end (small)
-@pytest.mark.parametrize("spec", SMALL + TINY, ids=_small_ids())
+@pytest.mark.parametrize("spec", SMALL + TINY + FEW, ids=_small_ids())
 def test_forward_small_all_outputs(spec):
     say(f"[forward small] {spec.name}")
     inp = W.generate(spec)
@@ -114,7 +126,8 @@ def test_forward_small_all_outputs(spec):
         assert np.all(as_f64(o["out"])[dropped] == 0.0)
 
 
-@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2], ids=lambda s: s.name)
+@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:2],
+                         ids=lambda s: s.name)
 def test_stages_equal_forward_bitwise(spec):
     say(f"[stages == forward] {spec.name}")
     inp = W.generate(spec)
@@ -207,7 +220,7 @@ def test_permute_stage(spec):
 
 
 @pytest.mark.parametrize("spec", [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[6], SMALL[7]]
-                         + SILU, ids=lambda s: s.name)
+                         + SILU + FEW, ids=lambda s: s.name)
 def test_expert_ffn_stage(spec):
     say(f"[expert_ffn] {spec.name}")
     inp = W.generate(spec)
