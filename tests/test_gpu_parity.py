@@ -97,12 +97,22 @@ FEW = [
 ]
 
 
+# Thousands of tokens through the narrow-gate router: a ragged H (the second
+# 256-wide stage half empty) and T (a last block of 8 tokens) with 16-bit gate
+# reads (E % 4 != 0), and E = 16 with k = 4.
+RES = [
+    S("router_T8200_H264_E6_k2_F128", 8200, 264, 6, 2, 128, biases=True),
+    S("router_T8192_H1024_E16_k4_F128_cf1.0", 8192, 1024, 16, 4, 128, cf=1.0,
+      wg=W.Dist("normal", 0.05)),
+]
+
+
 def _small_ids():
-    return [s.name for s in SMALL + TINY + FEW]
+    return [s.name for s in SMALL + TINY + FEW + RES]
 
 
 # ---------------------------------------------------------------- end to end (small)
-@pytest.mark.parametrize("spec", SMALL + TINY + FEW, ids=_small_ids())
+@pytest.mark.parametrize("spec", SMALL + TINY + FEW + RES, ids=_small_ids())
 def test_forward_small_all_outputs(spec):
     say(f"[forward small] {spec.name}")
     inp = W.generate(spec)
@@ -126,7 +136,7 @@ def test_forward_small_all_outputs(spec):
         assert np.all(as_f64(o["out"])[dropped] == 0.0)
 
 
-@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:2],
+@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:2] + RES[:1],
                          ids=lambda s: s.name)
 def test_stages_equal_forward_bitwise(spec):
     say(f"[stages == forward] {spec.name}")
