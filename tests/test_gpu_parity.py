@@ -107,12 +107,23 @@ RES = [
 ]
 
 
+# Every router shape by gate width: E in 17..32 with 16-bit gate reads
+# (E % 4 != 0) and with transposing reads, E not a multiple of 16 above 128,
+# and the widest gate (E = 256, k = 8) with drops.
+WIDE = [
+    S("wide_E17_T500_H136_k2_F64", 500, 136, 17, 2, 64, biases=True),
+    S("wide_E24_T700_H264_k3_F136_cf1.0", 700, 264, 24, 3, 136, cf=1.0),
+    S("wide_E200_T129_H512_k2_F64", 129, 512, 200, 2, 64, wg=W.Dist("normal", 0.1)),
+    S("wide_E256_T300_H128_k8_F128_cf1.0", 300, 128, 256, 8, 128, cf=1.0, biases=True),
+]
+
+
 def _small_ids():
-    return [s.name for s in SMALL + TINY + FEW + RES]
+    return [s.name for s in SMALL + TINY + FEW + RES + WIDE]
 
 
 # ---------------------------------------------------------------- end to end (small)
-@pytest.mark.parametrize("spec", SMALL + TINY + FEW + RES, ids=_small_ids())
+@pytest.mark.parametrize("spec", SMALL + TINY + FEW + RES + WIDE, ids=_small_ids())
 def test_forward_small_all_outputs(spec):
     say(f"[forward small] {spec.name}")
     inp = W.generate(spec)
@@ -136,7 +147,7 @@ def test_forward_small_all_outputs(spec):
         assert np.all(as_f64(o["out"])[dropped] == 0.0)
 
 
-@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:2] + RES[:1],
+@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:2] + RES[:1] + WIDE[1:2],
                          ids=lambda s: s.name)
 def test_stages_equal_forward_bitwise(spec):
     say(f"[stages == forward] {spec.name}")
