@@ -43,12 +43,14 @@ namespace {
 // ---------------------------------------------------------------- bf16 MFMA
 // k-tile depth and LDS stages: the 256-row layout takes 64-deep k-tiles in 2
 // stages (one barrier per 64 k, 128 KB of LDS); the narrower layouts, which
-// stream weights, keep 32-deep k-tiles in 4 stages (prefetch 3 k-tiles ahead).
-template <int BM>
+// stream weights, keep 32-deep k-tiles in 4 stages (prefetch 3 k-tiles ahead),
+// or NSV stages where a kernel overrides it (3 stages, 72 KB at 128 rows, so
+// that two workgroups share a CU).
+template <int BM, int NSV = 0>
 struct Cfg {
     static constexpr int BN = 256;
     static constexpr int BK = BM == 256 ? 64 : 32;    // k-tile depth
-    static constexpr int NS = BM == 256 ? 2 : 4;      // LDS stages
+    static constexpr int NS = NSV ? NSV : (BM == 256 ? 2 : 4);   // LDS stages
     static constexpr int WM = (BM == 256) ? 2 : 1;   // waves along m
     static constexpr int WN = 4 / WM;                // waves along n
     static constexpr int TN = BN / WN, TM = BM / WM; // per-wave extent
@@ -90,7 +92,7 @@ struct TailPlan {
     int S;            // slices per tail tile (1: no cut)
 };
 
-template <int BM>
+template <int BM, int NSV>
 __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int Nt,
                                               int ncu, int nk, bool allow) {
     TailPlan pl;
@@ -99,7 +101,7 @@ __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offset
     const int R = mtiles * Nt;
     pl.tail = R % ncu;
     int S = pl.tail > 0 ? min(ncu, kMaxUnits) / pl.tail : 1;
-    S = min(S, nk / Cfg<BM>::NS);
+    S = min(S, nk / Cfg<BM, NSV>::NS);
     if (!allow || S < 2) {
         pl.S = 1;
         pl.tail = 0;
@@ -128,12 +130,12 @@ struct TileRef {
 // DMA pipeline and MFMA loop over the k-tiles [kb, kb + nkr) of tile `tr`,
 // accumulating into acc (the caller zeroes it).  `lds` holds Cfg<BM>::LDS_BYTES.
 // NTW: weight loads carry the nontemporal hint (see ffn_gemm_bf16).
-template <int BM, bool NTW>
+template <int BM, bool NTW, int NSV>
 __device__ __forceinline__ void gemm_mainloop(
     const TileRef& tr, int kb, int nkr, char* lds, const uint16_t* __restrict__ X,
     uint32_t x_bytes, const int32_t* __restrict__ rowmap, const uint16_t* __restrict__ W, int K,
     int N, f32x16_t (&acc)[Cfg<BM>::FN][Cfg<BM>::FM]) {
-    using G = Cfg<BM>;
+    using G = Cfg<BM, NSV>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WN, wm = wave / G::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -518,7 +520,7 @@ __device__ __forceinline__ bool tile_ref(const int32_t* __restrict__ offsets, in
 }
 
 // One whole tile with the row layout of Cfg<TB> (TB <= the kernel's BM).
-template <int TB, int ACT, bool NTW, bool SAVE>
+template <int TB, int ACT, bool NTW, bool SAVE, int NSV>
 __device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
                                            const uint16_t* __restrict__ X, uint32_t x_bytes,
                                            const int32_t* __restrict__ rowmap,
@@ -530,7 +532,7 @@ __device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
     const int nk = (K + Cfg<TB>::BK - 1) / Cfg<TB>::BK;
     f32x16_t acc[Cfg<TB>::FN][Cfg<TB>::FM];
     zero_acc<TB>(acc);
-    gemm_mainloop<TB, NTW>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_mainloop<TB, NTW, NSV>(tr, 0, nk, lds, X, x_bytes, rowmap, W, K, N, acc);
     gemm_epilogue<TB, ACT, SAVE>(tr, acc, lds, bias, C, Cpre, N);
 }
 
@@ -538,24 +540,27 @@ __device__ __forceinline__ void whole_tile(const TileRef& tr, char* lds,
 // (nullable) is the fp32 slice buffer; without it no tile is cut.  The last
 // row tile of an expert is usually short: with at most 128 (64) real rows it
 // runs the 128-row (64-row) layout, whose four waves split the columns instead
-// of idling on rows that do not exist.
-template <int BM, int ACT, bool SAVE>
-__global__ __launch_bounds__(256) void ffn_gemm_bf16(
+// of idling on rows that do not exist.  NSV (0: the layout's own stage count)
+// overrides the LDS stages of every layout the kernel runs; with NSV the
+// kernel is built for two resident workgroups per CU, and `ncu` counts
+// workgroup slots (two per CU) for the round of tiles.
+template <int BM, int ACT, bool SAVE, int NSV>
+__global__ __launch_bounds__(256, NSV ? 2 : 1) void ffn_gemm_bf16(
     const uint16_t* __restrict__ X, uint32_t x_bytes, const int32_t* __restrict__ rowmap,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ W,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre,
     int K, int N, int Nt, int SBN, int ncu, float* __restrict__ part) {
-    using G = Cfg<BM>;
+    using G = Cfg<BM, NSV>;
     __shared__ __attribute__((aligned(1024))) char lds[G::LDS_BYTES];
-    static_assert(BM < 128 || Cfg<64>::LDS_BYTES <= G::LDS_BYTES, "64-row layout fits");
-    static_assert(BM < 256 || Cfg<128>::LDS_BYTES <= G::LDS_BYTES, "128-row layout fits");
+    static_assert(BM < 128 || Cfg<64, NSV>::LDS_BYTES <= G::LDS_BYTES, "64-row layout fits");
+    static_assert(BM < 256 || Cfg<128, NSV>::LDS_BYTES <= G::LDS_BYTES, "128-row layout fits");
     // With at most 128 rows per tile (few rows per expert) an expert's weights
     // are read about once, so they stream past the last-level cache instead of
     // evicting (and writing back) other kernels' lines; the 256-row layout
     // re-reads weight tiles across row tiles and keeps the default policy.
     constexpr bool kNtW = BM <= 128;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, part != nullptr);
+    const TailPlan pl = tail_plan<BM, NSV>(offsets, E, Nt, ncu, nk, part != nullptr);
     const int p = blockIdx.x;
     int tile = p, kb = 0, nkr = nk, unit = -1;
     if (p >= pl.full) {
@@ -575,24 +580,24 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16(
         const int rows = tr.n_rows - tr.m0;
         if constexpr (BM >= 128) {
             if (rows <= 64) {
-                whole_tile<64, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                whole_tile<64, ACT, kNtW, SAVE, NSV>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
                                                   N);
                 return;
             }
         }
         if constexpr (BM >= 256) {
             if (rows <= 128) {
-                whole_tile<128, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
+                whole_tile<128, ACT, kNtW, SAVE, NSV>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K,
                                                    N);
                 return;
             }
         }
-        whole_tile<BM, ACT, kNtW, SAVE>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
+        whole_tile<BM, ACT, kNtW, SAVE, NSV>(tr, lds, X, x_bytes, rowmap, W, bias, C, Cpre, K, N);
         return;
     }
     f32x16_t acc[G::FN][G::FM];
     zero_acc<BM>(acc);
-    gemm_mainloop<BM, kNtW>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
+    gemm_mainloop<BM, kNtW, NSV>(tr, kb, nkr, lds, X, x_bytes, rowmap, W, K, N, acc);
     store_partial<BM>(acc, part + (int64_t)unit * G::UNIT, tr.n_rows - tr.m0);
 }
 
@@ -608,14 +613,14 @@ struct FixCfg {
     static constexpr int BATCH = 8;                       // slice loads in flight
 };
 
-template <int BM, int ACT>
+template <int BM, int ACT, int NSV>
 __global__ __launch_bounds__(256) void ffn_gemm_fixup(
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ C, uint16_t* __restrict__ Cpre, int K, int N, int Nt, int SBN, int ncu,
     const float* __restrict__ part) {
-    using G = Cfg<BM>;
+    using G = Cfg<BM, NSV>;
     const int nk = (K + G::BK - 1) / G::BK;
-    const TailPlan pl = tail_plan<BM>(offsets, E, Nt, ncu, nk, true);
+    const TailPlan pl = tail_plan<BM, NSV>(offsets, E, Nt, ncu, nk, true);
     const int i = blockIdx.x / FixCfg<BM>::CHUNKS, c = blockIdx.x % FixCfg<BM>::CHUNKS;
     if (pl.S < 2 || i >= pl.tail) return;
     int mt, nt;
@@ -755,27 +760,51 @@ int pick_bm(const moe_problem_t& p) {
 int gemm_nt(int N) { return (N + 255) / 256; }
 
 // Every real tile, plus room for one round of K slices; the fixup covers at
-// most half a round of tail tiles (each is cut in 2 or more).
-template <int BM, int ACT>
+// most half a round of tail tiles (each is cut in 2 or more).  `slots`:
+// workgroups resident at once (CUs, or twice that with NSV).
+template <int BM, int ACT, int NSV>
 hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
                  int E, const uint16_t* w, const uint16_t* b, uint16_t* c, uint16_t* cpre, int K,
-                 int N, int Mt, int Nt, int SBN, int ncu, float* part, hipEvent_t mid,
+                 int N, int Mt, int Nt, int SBN, int slots, float* part, hipEvent_t mid,
                  hipStream_t s) {
-    const int units = std::min(ncu, kMaxUnits);
+    const int units = std::min(slots, kMaxUnits);
     const dim3 block(256), grid((unsigned)((int64_t)Mt * Nt + units));
     if (cpre)
-        ffn_gemm_bf16<BM, ACT, true><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b, c,
-                                                            cpre, K, N, Nt, SBN, ncu, part);
+        ffn_gemm_bf16<BM, ACT, true, NSV><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b,
+                                                                 c, cpre, K, N, Nt, SBN, slots,
+                                                                 part);
     else
-        ffn_gemm_bf16<BM, ACT, false><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b, c,
-                                                             nullptr, K, N, Nt, SBN, ncu, part);
+        ffn_gemm_bf16<BM, ACT, false, NSV><<<grid, block, 0, s>>>(x, xb, rowmap, offsets, E, w, b,
+                                                                  c, nullptr, K, N, Nt, SBN, slots,
+                                                                  part);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
     if (part)
-        ffn_gemm_fixup<BM, ACT><<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
-            offsets, E, b, c, cpre, K, N, Nt, SBN, ncu, part);
+        ffn_gemm_fixup<BM, ACT, NSV>
+            <<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
+                offsets, E, b, c, cpre, K, N, Nt, SBN, slots, part);
     return hipGetLastError();
+}
+
+// Two resident workgroups per CU (3 LDS stages each, 72 KB) for the first
+// GEMM when its tiles have 128 rows: with a few dozen rows per expert it
+// streams weights, and two workgroups keep twice the DMAs in flight per CU
+// while each other's epilogue runs (10 % off that launch on a 128-expert top-1
+// layer, 5 % on a 256-token decode batch).  The second GEMM, and the 64-row
+// layout, measured slower or unchanged that way.  MOE_GEMM_DUAL (a build
+// switch for such comparisons) 0: never; 1: this rule; 2: the first GEMM at
+// 64 or 128 rows; 3: both GEMMs at 64 or 128 rows.
+#ifndef MOE_GEMM_DUAL
+#define MOE_GEMM_DUAL 1
+#endif
+bool gemm_dual(int bm, bool first) {
+    switch (MOE_GEMM_DUAL) {
+    case 1: return first && bm == 128;
+    case 2: return first && bm <= 128;
+    case 3: return bm <= 128;
+    default: return false;
+    }
 }
 
 template <int ACT>
@@ -799,15 +828,22 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         const int64_t xrows = rowmap ? p.T : rows;
         const uint32_t xb = (uint32_t)(xrows * K * 2);
         hipError_t e;
+        const bool dual = gemm_dual(bm, ACT != kActNone);
         if (bm == 256)
-            e = launch_bf16<256, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
-                                  mid, s);
+            e = launch_bf16<256, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
+                                         SBN, ncu, part, mid, s);
+        else if (bm == 128 && dual)
+            e = launch_bf16<128, ACT, 3>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
+                                         SBN, 2 * ncu, part, mid, s);
         else if (bm == 128)
-            e = launch_bf16<128, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
-                                  mid, s);
+            e = launch_bf16<128, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
+                                         SBN, ncu, part, mid, s);
+        else if (dual)
+            e = launch_bf16<64, ACT, 3>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN,
+                                        2 * ncu, part, mid, s);
         else
-            e = launch_bf16<64, ACT>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN, ncu, part,
-                                 mid, s);
+            e = launch_bf16<64, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN,
+                                        ncu, part, mid, s);
         return e;
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
