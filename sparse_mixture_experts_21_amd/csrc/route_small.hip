@@ -7,10 +7,11 @@
 // the router and the two dispatch kernels do is one launch:
 //   1. logits l[t][e] = x[t] . Wg[:, e] (+ bg[e]) in fp32.  x and the gate
 //      columns are staged in LDS (all of H at once when T + E rows of it fit
-//      in 130 KB, else in blocks); the TP threads of a
-//      (token, expert) pair each add the 8-element chunks c = hp, hp + TP, ...
-//      of every block, then the pair's TP partial sums are added in a fixed
-//      order (a butterfly within the wave, then the waves in order);
+//      in 130 KB, else in blocks); with few pairs, 32 or more threads per
+//      (token, expert) pair add 8-element chunks, the partial sums added in a
+//      fixed order; with 32 pairs or more, 16 x 16 tiles of them on MFMA,
+//      the 16 waves taking every 16th 32-wide k-step of each block, then the
+//      waves' partial tiles added in wave order;
 //   2. per token (one wave, a lane per expert): softmax, top-k on the logits
 //      (descending, equal logits to the lower expert), the k probabilities
 //      renormalised to sum to one, lse;
@@ -30,7 +31,9 @@ namespace {
 
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallLds = 66560;       // bf16 elements of the x / gate staging (130 KB)
+constexpr int kSmallMfmaPairs = 32;    // from this many (token, expert) pairs on, MFMA logits
 
+template <bool MFMA>
 __global__ __launch_bounds__(kSmallThreads) void route_small(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg,
     const uint16_t* __restrict__ bg, int T, int H, int E, int k, int32_t cap,
@@ -50,14 +53,25 @@ __global__ __launch_bounds__(kSmallThreads) void route_small(
     const int HB = min(H, (kSmallLds / (T + E) - 8) & ~7);
     const int PITCH = HB + 8;
     uint16_t* ws = xs + T * PITCH;
-    // threads per pair: a power of two, >= 16
+    // Fewer than kSmallMfmaPairs pairs: TP >= 32 threads per pair each add
+    // 8-element chunks c = hp, hp + TP, ... of every block, then a butterfly
+    // within the wave and the waves in order.  More: logit tiles of 16 tokens
+    // x 16 experts on v_mfma_f32_16x16x32_bf16 (A: lane l holds 8 consecutive
+    // h of token row l % 16, B: of expert column l % 16, both straight from the
+    // staged rows; T * E <= 64 makes at most four tiles), the 16 waves taking
+    // every 16th 32-wide k-step of each block, then their partial tiles added
+    // in wave order.
+    constexpr bool mfma = MFMA;              // the host picks it: NP >= kSmallMfmaPairs
     int TP = kSmallThreads;
     while (TP * NP > kSmallThreads) TP >>= 1;
     const int p = tid / TP, hp = tid % TP;     // pair p = t * E + e (p < NP when active)
-    const int t = p / E, e = p % E;
-    const bool active = p < NP;
-
-    float acc = 0.f;
+    const bool active = !mfma && p < NP;
+    float fac = 0.f;
+    const int TT = (T + 15) / 16, ET = (E + 15) / 16, NTL = TT * ET;
+    const int l16 = lane & 15, kg = lane >> 4;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int h0 = 0; h0 < H; h0 += HB) {
         const int hb = min(HB, H - h0);        // a multiple of 8
         const int nch = hb / 8;
@@ -95,24 +109,59 @@ __global__ __launch_bounds__(kSmallThreads) void route_small(
         }
         __syncthreads();
         if (active) {
+            const int t = p / E, e = p % E;
             for (int c = hp; c < nch; c += TP) {
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + t * PITCH + 8 * c);
                 const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(ws + e * PITCH + 8 * c);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    acc = fmaf(bf16_lo(xv[q]), bf16_lo(wv[q]), acc);
-                    acc = fmaf(bf16_hi(xv[q]), bf16_hi(wv[q]), acc);
+                    fac = fmaf(bf16_lo(xv[q]), bf16_lo(wv[q]), fac);
+                    fac = fmaf(bf16_hi(xv[q]), bf16_hi(wv[q]), fac);
                 }
             }
         }
+        const int nks = mfma ? (hb + 31) / 32 : 0;
+        for (int ks = wave; ks < nks; ks += kSmallThreads / 64) {
+            const int kc = ks * 32 + kg * 8;              // this lane's 8 h of the block
+            const bool kin = kc < hb;                     // hb % 8 == 0: all 8 or none
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q >= NTL) break;                      // uniform
+                const int tr = (q / ET) * 16 + l16, er = (q % ET) * 16 + l16;
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                const u32x4_t av =
+                    (kin && tr < T) ? *reinterpret_cast<const u32x4_t*>(xs + tr * PITCH + kc) : z;
+                const u32x4_t bv =
+                    (kin && er < E) ? *reinterpret_cast<const u32x4_t*>(ws + er * PITCH + kc) : z;
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc[q],
+                    0, 0, 0);
+            }
+        }
     }
-    // the pair's TP partials: butterfly over min(TP, 64) lanes, then waves in order
-    const int TW = min(TP, 64);
-    for (int d = TW >> 1; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    if (active && (lane % TW) == 0) part[wave][p] = acc;   // one value per (wave, pair)
+    if (!mfma) {
+        // the pair's TP partials: butterfly over min(TP, 64) lanes, then waves in order
+        const int TW = min(TP, 64);
+        for (int d = TW >> 1; d >= 1; d >>= 1) fac += __shfl_xor(fac, d);
+        if (active && (lane % TW) == 0) part[wave][p] = fac;   // one value per (wave, pair)
+    } else {
+        // each wave's partial of every pair (lane l holds tokens 4 (l / 16) + i
+        // of expert column l % 16 of each tile)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q >= NTL) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tq = (q / ET) * 16 + 4 * kg + i, eq = (q % ET) * 16 + l16;
+                if (tq < T && eq < E) part[wave][tq * E + eq] = acc[q][i];
+            }
+        }
+    }
     __syncthreads();
     if (tid < NP) {
-        const int w0 = tid * TP / 64, nw = TP > 64 ? TP / 64 : 1;
+        // the waves that hold the pair's partials, in order
+        const int w0 = mfma ? 0 : tid * TP / 64;
+        const int nw = mfma ? kSmallThreads / 64 : (TP > 64 ? TP / 64 : 1);
         float sum = part[w0][tid];
         for (int w = 1; w < nw; ++w) sum += part[w0 + w][tid];
         if (bg) sum += bf16_lo((uint32_t)bg[tid % E]);
@@ -233,10 +282,17 @@ hipError_t launch_route_small(const moe_problem_t& p, int64_t cap, const void* x
                               int32_t* counts, float* losses, int32_t* offsets, int32_t* pos,
                               int32_t* row_token, hipStream_t s) {
     const int32_t c = (int32_t)std::min<int64_t>(cap, INT32_MAX);
-    route_small<<<dim3(1), dim3(kSmallThreads), 0, s>>>(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
-        static_cast<const uint16_t*>(bg), (int)p.T, p.H, p.E, p.k, c, logits, topk_idx, topk_w,
-        counts, losses, offsets, pos, row_token);
+    auto* xb = static_cast<const uint16_t*>(x);
+    auto* wb = static_cast<const uint16_t*>(Wg);
+    auto* bb = static_cast<const uint16_t*>(bg);
+    if (p.T * (int64_t)p.E >= kSmallMfmaPairs)
+        route_small<true><<<dim3(1), dim3(kSmallThreads), 0, s>>>(
+            xb, wb, bb, (int)p.T, p.H, p.E, p.k, c, logits, topk_idx, topk_w, counts, losses,
+            offsets, pos, row_token);
+    else
+        route_small<false><<<dim3(1), dim3(kSmallThreads), 0, s>>>(
+            xb, wb, bb, (int)p.T, p.H, p.E, p.k, c, logits, topk_idx, topk_w, counts, losses,
+            offsets, pos, row_token);
     return hipGetLastError();
 }
 
