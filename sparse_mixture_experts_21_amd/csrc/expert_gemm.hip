@@ -21,14 +21,15 @@
 // consecutive output columns (8-byte stores).  Operands move HBM -> LDS with
 // buffer_load ... lds (no VGPR staging) through a ring of LDS stages (2 of
 // 64-deep k-tiles for 256-row tiles, 4 of 32-deep ones for the narrower
-// layouts), issued NS - 1 k-tiles ahead of the MFMAs.  The weights stay in their
+// layouts, or 3 when two workgroups share a CU), issued NS - 1 k-tiles ahead
+// of the MFMAs.  The weights stay in their
 // natural [k][n] layout in LDS and are turned into K-contiguous MFMA
 // fragments by ds_read_b64_tr_b16; the rows of X are [m][k] in LDS.  LDS
 // fragment reads for the next k-substep are interleaved with the MFMAs of
 // the current one, and one barrier per k-tile orders DMA and reads.
 //
 // Load balance: when the real tiles leave a ragged last round of at most half
-// the CUs, those tiles are cut along K into slices that fill one whole round
+// the workgroup slots, those tiles are cut along K into slices that fill one whole round
 // and write fp32 partials; ffn_gemm_fixup sums them in slice order and applies
 // the epilogue (bias, activation, bf16).
 #include <type_traits>
