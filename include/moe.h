@@ -89,7 +89,9 @@ typedef struct {
  * final stage.  MOE_EV_FFN_UP and MOE_EV_FFN_DOWN start the two expert GEMM
  * launches alone; the *_FIXUP stages that follow each sum the K slices of the
  * tiles cut in its last round and apply the epilogue to them (empty when no
- * tile is cut). */
+ * tile is cut).  A NULL entry skips that point: every recorded event adds a
+ * few microseconds between two kernels, so a caller timing one stage records
+ * only its two events. */
 enum {
     MOE_EV_ROUTE = 0,
     MOE_EV_PERMUTE = 1,
@@ -288,7 +290,8 @@ moe_status_t moe_forward_train(const moe_problem_t* p, const void* x, const void
                                size_t ws_bytes, hipStream_t stream);
 
 /* Events recorded by moe_backward when `stage_events` is non-NULL, event i
- * just before stage i starts, the last after the final stage. */
+ * just before stage i starts, the last after the final stage (a NULL entry
+ * skips that point). */
 enum {
     MOE_BEV_TOKEN = 0,       /* dw, dy rows, the router's dl */
     MOE_BEV_DGRAD_DA = 1,    /* da = (dy W2^T) * act'(a), act'(a) saved  (one GEMM launch) */

@@ -307,11 +307,13 @@ class StageEvents:
     via events=...: the library records them on its stream around each stage,
     so stage times come from the stream the kernels actually run on."""
 
-    def __init__(self, n: int = MOE_FORWARD_EVENTS):
+    def __init__(self, n: int = MOE_FORWARD_EVENTS, points: Optional[Sequence[int]] = None):
+        """points: the event indices to record (default all); the others are
+        NULL, which the library skips."""
         h = _hiprt()
         self.n = n
         self._ev = (ctypes.c_void_p * n)()
-        for i in range(n):
+        for i in (range(n) if points is None else points):
             e = ctypes.c_void_p()
             if h.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -320,17 +322,19 @@ class StageEvents:
     def array(self):
         return self._ev
 
-    def stage_ms(self) -> Sequence[float]:
-        """Milliseconds of each stage of the last recorded call (waits for it)."""
+    def elapsed_ms(self, i: int, j: int) -> float:
+        """Milliseconds from event i to event j of the last recorded call."""
         h = _hiprt()
-        h.hipEventSynchronize(self._ev[self.n - 1])
-        out = []
-        for i in range(self.n - 1):
-            ms = ctypes.c_float()
-            if h.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[i + 1]) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            out.append(ms.value)
-        return out
+        h.hipEventSynchronize(self._ev[j])
+        ms = ctypes.c_float()
+        if h.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def stage_ms(self) -> Sequence[float]:
+        """Milliseconds of each stage of the last recorded call (waits for it;
+        every event must have been recorded)."""
+        return [self.elapsed_ms(i, i + 1) for i in range(self.n - 1)]
 
     def __del__(self):
         try:

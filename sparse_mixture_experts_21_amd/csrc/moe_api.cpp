@@ -247,7 +247,8 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     void* y = w + L.y;
 
     auto ev = [&](int i) -> hipError_t {
-        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+        return stage_events && stage_events[i] ? hipEventRecord(stage_events[i], stream)
+                                              : hipSuccess;
     };
     hipError_t e = ev(MOE_EV_ROUTE);
     if (route_small_fits(*p)) {
@@ -441,10 +442,6 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const void* Wg, 
     moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (!x || !Wg || !W1 || !W2 || !out || !losses || !ws) return MOE_ERR_INVALID_ARG;
-    if (stage_events) {
-        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
-            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    }
     if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
         !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !aligned16(losses) ||
         !opt_ok(logits) || !opt_ok(topk_idx) || !opt_ok(topk_w) || !opt_ok(counts) ||
@@ -466,10 +463,6 @@ moe_status_t moe_forward_noalloc(const moe_problem_t* p, const void* x, const vo
     moe_status_t st = check_problem(p);
     if (st != MOE_OK) return st;
     if (!x || !Wg || !W1 || !W2 || !out || !losses) return MOE_ERR_INVALID_ARG;
-    if (stage_events) {
-        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
-            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    }
     if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
         !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !aligned16(losses) ||
         !opt_ok(logits) || !opt_ok(topk_idx) || !opt_ok(topk_w) || !opt_ok(counts) ||
@@ -538,10 +531,6 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, co
     moe_status_t st = check_group(p, group);
     if (st != MOE_OK) return st;
     if (!x || !Wg || !W1 || !W2 || !out || !ws) return MOE_ERR_INVALID_ARG;
-    if (stage_events) {
-        for (int i = 0; i < MOE_FORWARD_EVENTS; ++i)
-            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    }
     if (!aligned16(x) || !aligned16(Wg) || !opt_ok(bg) || !aligned16(W1) || !opt_ok(b1) ||
         !aligned16(W2) || !opt_ok(b2) || !aligned16(out) || !opt_ok(logits) || !opt_ok(probs) ||
         !opt_ok(sel) || !opt_ok(rowof) || !aligned16(ws))
@@ -561,7 +550,8 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, int64_t group, co
     pc.k = p->E;
 
     auto ev = [&](int i) -> hipError_t {
-        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+        return stage_events && stage_events[i] ? hipEventRecord(stage_events[i], stream)
+                                              : hipSuccess;
     };
     hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
     hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
@@ -617,10 +607,6 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg,
     if (st != MOE_OK) return st;
     if (!x || !Wg || !W1 || !W2 || !dout || !dx || !dWg || !dW1 || !dW2 || !ws)
         return MOE_ERR_INVALID_ARG;
-    if (stage_events) {
-        for (int i = 0; i < MOE_BACKWARD_EVENTS; ++i)
-            if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    }
     if (std::isnan(g_aux) || std::isnan(g_z)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(Wg) || !aligned16(W1) || !aligned16(W2) || !aligned16(dout) ||
         !aligned16(dx) || !aligned16(dWg) || !opt_ok(dbg) || !aligned16(dW1) || !opt_ok(db1) ||
@@ -644,7 +630,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const void* Wg,
     const int H = p->H, F = p->F;
 
     auto ev = [&](int i) -> hipError_t {
-        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+        return stage_events && stage_events[i] ? hipEventRecord(stage_events[i], stream)
+                                              : hipSuccess;
     };
     // dw, dy rows and the router's dl; then the two data-gradient GEMMs and dx
     hipError_t e = ev(MOE_BEV_TOKEN);

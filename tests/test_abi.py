@@ -207,9 +207,15 @@ def test_forward_workspace_exact_size():
     assert forward(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
 
 
-def test_forward_null_event_in_array():
+def test_forward_null_event_entries_are_skipped_not_rejected():
+    """A NULL entry of stage_events skips that point: validation accepts an
+    array of NULLs and goes on to the next check (here the workspace size),
+    so nothing is launched."""
     arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
-    assert forward(P(), ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+    p = P()
+    need = moe.moe_workspace_bytes(p)
+    assert forward(p, ev=ctypes.cast(arr, ctypes.c_void_p), ws_bytes=need - 1) == \
+        moe.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("T,k,E,cf,cap", [
@@ -306,14 +312,16 @@ def test_ec_forward_misaligned(arg):
     assert ec_forward(P(), 64, **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
 
 
-def test_ec_workspace_exact_size_and_null_event():
+def test_ec_workspace_exact_size_and_null_events():
     p = P()
     need = moe.moe_ec_workspace_bytes(p, 64)
     assert need % 256 == 0 and need > 0
     assert ec_forward(p, 64, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert ec_route(p, 64, ws_bytes=0) == moe.MOE_ERR_WORKSPACE
+    # NULL event entries are skipped, not rejected: validation reaches the workspace check
     arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
-    assert ec_forward(p, 64, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+    assert ec_forward(p, 64, ev=ctypes.cast(arr, ctypes.c_void_p), ws_bytes=need - 1) == \
+        moe.MOE_ERR_WORKSPACE
 
 
 # ---------------------------------------------------------------- training
@@ -368,8 +376,10 @@ def test_train_workspace_sizes_and_nan_weights():
     assert fwd_train(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert bwd(p, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert bwd(p, g_aux=math.nan) == moe.MOE_ERR_INVALID_ARG
+    # NULL event entries are skipped, not rejected: validation reaches the workspace check
     arr = (ctypes.c_void_p * moe.MOE_BACKWARD_EVENTS)()
-    assert bwd(p, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+    assert bwd(p, ev=ctypes.cast(arr, ctypes.c_void_p), ws_bytes=need - 1) == \
+        moe.MOE_ERR_WORKSPACE
 
 
 # ---------------------------------------------------------------- fixed scratch
@@ -394,13 +404,14 @@ def test_noalloc_null_and_misaligned(arg):
     assert fwd_noalloc(P(), **{arg: MIS}) == moe.MOE_ERR_UNSUPPORTED
 
 
-def test_noalloc_scratch_limit_and_null_event():
+def test_noalloc_scratch_limit_and_null_events():
     """A problem whose workspace exceeds the fixed scratch is refused with
-    MOE_ERR_WORKSPACE before any HIP call (this runs without a GPU)."""
+    MOE_ERR_WORKSPACE before any HIP call (this runs without a GPU), also
+    with an event array of NULL entries (skipped, not rejected)."""
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
     big = P(T=8192, H=1024, E=8, k=2, F=4096)
     assert moe.moe_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
     assert fwd_noalloc(big) == moe.MOE_ERR_WORKSPACE
     arr = (ctypes.c_void_p * moe.MOE_FORWARD_EVENTS)()
-    assert fwd_noalloc(P(), ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_INVALID_ARG
+    assert fwd_noalloc(big, ev=ctypes.cast(arr, ctypes.c_void_p)) == moe.MOE_ERR_WORKSPACE
