@@ -1,0 +1,132 @@
+"""Host logic of bench.py, on the CPU: kernel names as the counter summaries key
+them, the calibration of FETCH_SIZE / WRITE_SIZE by the copy kernel, the
+source-hash guard on stored traffic, the routing statistics, and the refusal
+of more than one GPU."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("symbol,key", [
+    ("void moe::(anonymous namespace)::ffn_gemm_bf16<256, 1, false, 0>(unsigned short const*)",
+     "ffn_gemm_bf16_up"),
+    ("void moe::(anonymous namespace)::ffn_gemm_bf16<256, 2, true, 0>(unsigned short const*)",
+     "ffn_gemm_bf16_up"),
+    ("void moe::(anonymous namespace)::ffn_gemm_bf16<128, 0, false, 3>(unsigned short const*)",
+     "ffn_gemm_bf16_down"),
+    ("ffn_gemm_bf16<64, 0, false, 0>", "ffn_gemm_bf16_down"),
+    ("void moe::(anonymous namespace)::route_bf16<1, 16, 256, 3, 8, false>(int)", "route_bf16"),
+    ("void moe::(anonymous namespace)::combine_rows<true, 256>(float const*)", "combine_rows"),
+    ("void moe::(anonymous namespace)::ffn_gemm_fixup<256, 1, 0>(int const*)", "ffn_gemm_fixup"),
+    ("scan_columns", "scan_columns"),
+])
+def test_kernel_key(symbol, key):
+    assert bench.kernel_key(symbol) == key
+
+
+def _pmc_dir(tmp_path, name, counter, rows):
+    d = tmp_path / name / "host" / "pid"
+    d.mkdir(parents=True)
+    with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name",
+                                           "Counter_Value"])
+        w.writeheader()
+        for kname, grid, value in rows:
+            w.writerow({"Kernel_Name": kname, "Grid_Size": grid, "Counter_Name": counter,
+                        "Counter_Value": value})
+        # a row of another counter in the same file is ignored
+        w.writerow({"Kernel_Name": "combine_rows<true, 256>", "Grid_Size": 1,
+                    "Counter_Name": "GRBM_COUNT", "Counter_Value": 1e9})
+    return str(tmp_path / name)
+
+
+def test_summarize_pmc_calibrates_by_the_largest_copy(tmp_path):
+    up = "void moe::(anonymous namespace)::ffn_gemm_bf16<256, 1, false, 0>(x)"
+    dn = "void moe::(anonymous namespace)::ffn_gemm_bf16<256, 0, false, 0>(x)"
+    kib = 256 * 1024.0
+    fetch = _pmc_dir(tmp_path, "fetch", "FETCH_SIZE", [
+        ("__amd_rocclr_copyBuffer", 1024, 0.1 * kib),        # a small copy: not the calibration
+        ("__amd_rocclr_copyBuffer", 1 << 20, 0.5 * kib),     # the 256 MiB copy: factor 0.5
+        ("fill_kernel", 4096, 123.0),                        # fills are skipped
+        (up, 7448, 1000.0), (up, 7448, 3000.0),              # mean 2000 KiB
+        (dn, 2128, 500.0)])
+    write = _pmc_dir(tmp_path, "write", "WRITE_SIZE", [
+        ("__amd_rocclr_copyBuffer", 1 << 20, 1.0 * kib),     # factor 1.0
+        (up, 7448, 400.0), (up, 7448, 600.0)])               # mean 500 KiB; down writes none
+    out, lines = bench.summarize_pmc(fetch, write, "wl", 256)
+    assert out["workload"] == "wl" and out["source_hash"] == bench.kernel_source_hash()
+    assert out["fetch_factor"] == pytest.approx(0.5) and out["write_factor"] == pytest.approx(1.0)
+    assert set(out["kernels"]) == {"ffn_gemm_bf16_up", "ffn_gemm_bf16_down"}
+    u, d = out["kernels"]["ffn_gemm_bf16_up"], out["kernels"]["ffn_gemm_bf16_down"]
+    assert u["fetch_kib"] == pytest.approx(2000.0) and u["write_kib"] == pytest.approx(500.0)
+    assert u["hbm_bytes"] == pytest.approx((2000.0 / 0.5 + 500.0 / 1.0) * 1024.0)
+    assert d["write_kib"] is None and d["hbm_bytes"] == pytest.approx(500.0 / 0.5 * 1024.0)
+    # the table lists the larger fetch first
+    assert lines[2].startswith("| ffn_gemm_bf16_up |") and len(lines) == 4
+
+
+def test_summarize_pmc_needs_the_calibration_copy(tmp_path):
+    fetch = _pmc_dir(tmp_path, "fetch", "FETCH_SIZE", [("combine_rows<true, 256>", 1, 5.0)])
+    write = _pmc_dir(tmp_path, "write", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 9, 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(fetch, write, "wl", 256)
+
+
+def test_traffic_is_reported_only_for_the_same_sources_and_workload(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = {"source_hash": bench.kernel_source_hash(), "workload": "wl",
+           "kernels": {"ffn_gemm_bf16_up": {"hbm_bytes": 1.5e9}}}
+    with open(tmp_path / "traffic_wl.json", "w") as fh:
+        json.dump(rec, fh)
+    assert bench.traffic_for("ffn_gemm_bf16_up", "wl") == 1.5e9
+    assert bench.traffic_for("combine_rows", "wl") is None          # not measured
+    assert bench.traffic_for("ffn_gemm_bf16_up", "other") is None   # no file
+    rec["source_hash"] = "0" * 16                                   # other sources
+    with open(tmp_path / "traffic_wl.json", "w") as fh:
+        json.dump(rec, fh)
+    assert bench.traffic_for("ffn_gemm_bf16_up", "wl") is None
+    rec["source_hash"], rec["workload"] = bench.kernel_source_hash(), "other"
+    with open(tmp_path / "traffic_wl.json", "w") as fh:
+        json.dump(rec, fh)
+    assert bench.traffic_for("ffn_gemm_bf16_up", "wl") is None
+
+
+def test_source_hash_follows_every_library_source(tmp_path, monkeypatch):
+    csrc = tmp_path / "sparse_mixture_experts_21_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "a.hip").write_text("kernel a\n")
+    (csrc / "b.h").write_text("header b\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    assert h0 == bench.kernel_source_hash() and len(h0) == 16
+    (csrc / "b.h").write_text("header b changed\n")
+    h1 = bench.kernel_source_hash()
+    (csrc / "c.cpp").write_text("")
+    h2 = bench.kernel_source_hash()
+    assert len({h0, h1, h2}) == 3
+
+
+def test_routing_stats():
+    # E = 4, T = 6, k = 2: loads 5, 4, 3, 0 before capacity 4
+    counts = [5, 4, 3, 0]
+    offsets = np.cumsum([0, 4, 4, 3, 0])
+    s = bench.routing_stats(4, counts, offsets, 4, 6, 2)
+    assert s == {"load_max": 5, "load_min": 0, "kept_max": 4, "kept_min": 0,
+                 "experts_empty": 1, "capacity": 4, "dropped_pairs": 1,
+                 "drop_fraction": pytest.approx(1 / 12)}
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
