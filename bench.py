@@ -57,6 +57,11 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device-to-device copy of MIB MiB "
                          "(the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--vendor-gemm", type=float, default=0.0, metavar="SECONDS",
+                    help="instead of the layer: time the vendor library's batched GEMM "
+                         "(torch.bmm, hipBLASLt) on the workload's two expert GEMM shapes with "
+                         "balanced experts, each for about SECONDS, one JSON line (a side "
+                         "reference for the expert GEMMs; the library is not called)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE, both with --calibrate-copy) into "
@@ -152,6 +157,41 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int =
         out["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write.get(k), "hbm_bytes": hbm}
         lines.append(f"| {k} | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {hbm:.4g} |")
     return out, lines
+
+
+def vendor_gemm(spec, seconds: float):
+    """torch.bmm (hipBLASLt) on the expert GEMM shapes of `spec` with every
+    expert holding T k / E rows: [E, M, H] x [E, H, F] and [E, M, F] x [E, F, H]
+    in bf16, inputs drawn like the layer's (rows N(0, 1), weights N(0, 0.02)).
+    No activation, no gather and no ragged groups, so it is a plain batched
+    GEMM of the same flops: context for the expert GEMMs' rate, not the path."""
+    import torch
+    E, H, F = spec.E, spec.H, spec.F
+    M = spec.T * spec.k // E
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    res = {"workload": spec.name, "rows_per_expert": M, "kernel": "torch.bmm (hipBLASLt)"}
+    for name, (K, N) in (("up", (H, F)), ("down", (F, H))):
+        a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+        c = torch.bmm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, t0 = 0, time.perf_counter()
+        e0.record()
+        while n < 3 or time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                torch.bmm(a, b, out=c)
+            n += 10
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        flops = 2.0 * E * M * K * N
+        res[name] = {"calls": n, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+                     "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del a, b, c
+    return res
 
 
 def cpu_baseline(spec, inp, limit_s: float):
@@ -466,9 +506,12 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    spec = W.CONFIGS[args.config]
+    if args.vendor_gemm > 0:
+        print(json.dumps(vendor_gemm(spec, args.vendor_gemm)), flush=True)
+        return
     moe.lib()
 
-    spec = W.CONFIGS[args.config]
     T, H, E, k, F = spec.T, spec.H, spec.E, spec.k, spec.F
     log(f"[bench] generating {spec.name}")
     t0 = time.perf_counter()
@@ -622,10 +665,13 @@ def main():
                "frac": alg_bytes[n] / (sm[n] * 1e-3) / 1e9 / PEAK_HBM_GBS} for n in alg_bytes}
     # calibrated FETCH + WRITE bytes of the stage's kernels from profiles/, when
     # they were taken on these sources and this workload
+    # (each entry: the stage's kernels; a tuple names alternatives, the first
+    # one measured counts: the combine that finishes the cut tiles, or the plain one)
     stage_kernels = {"route": ("route_bf16",), "permute": ("scan_columns", "chunk_rank"),
-                     "combine": ("combine_rows",)}
+                     "combine": (("combine_rows_cut", "combine_rows"),)}
     for n, ks in stage_kernels.items():
-        tr = [traffic_for(kk, spec.name) for kk in ks]
+        tr = [next((v for v in (traffic_for(a, spec.name) for a in kk) if v is not None), None)
+              if isinstance(kk, tuple) else traffic_for(kk, spec.name) for kk in ks]
         if n in hbm:
             hbm[n]["traffic"] = None if g or any(v is None for v in tr) else sum(tr)
     kern = "ffn_gemm_bf16_up" if dom == "ffn_up" else "ffn_gemm_bf16_down"

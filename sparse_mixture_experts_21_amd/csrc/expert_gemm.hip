@@ -78,39 +78,14 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
 // The last (R mod ncu) tiles would leave most CUs idle in a final, ragged
-// round.  When they are at most half a round, each of them is cut along K into
-// S = ncu / tail slices (at most kMaxUnits slices in all, each at least NS
-// k-tiles deep): the slices form one full round and write fp32 partial rows,
-// which ffn_gemm_fixup sums in slice order before the epilogue.  Few tiles
-// (a few tokens per expert) are the same case: every tile is a tail tile, and
-// the partials cover only the tiles' real rows.
-constexpr int kMaxUnits = 256;
-
-struct TailPlan {
-    int real_mt;      // real row tiles
-    int full;         // tiles computed whole: positions [0, full)
-    int tail;         // tiles cut into S slices: positions [full, full + tail S)
-    int S;            // slices per tail tile (1: no cut)
-};
-
+// round: plan_tail cuts them along K when they are at most half a round.  Few
+// tiles (a few tokens per expert) are the same case: every tile is a tail
+// tile, and the partials cover only the tiles' real rows.
 template <int BM, int NSV>
 __device__ __forceinline__ TailPlan tail_plan(const int32_t* __restrict__ offsets, int E, int Nt,
                                               int ncu, int nk, bool allow) {
-    TailPlan pl;
     const int mtiles = __builtin_amdgcn_readfirstlane(real_row_tiles<BM>(offsets, E));
-    pl.real_mt = mtiles;
-    const int R = mtiles * Nt;
-    pl.tail = R % ncu;
-    int S = pl.tail > 0 ? min(ncu, kMaxUnits) / pl.tail : 1;
-    S = min(S, nk / Cfg<BM, NSV>::NS);
-    if (!allow || S < 2) {
-        pl.S = 1;
-        pl.tail = 0;
-    } else {
-        pl.S = S;
-    }
-    pl.full = R - pl.tail;
-    return pl;
+    return plan_tail(mtiles, Nt, ncu, nk, Cfg<BM, NSV>::NS, allow);
 }
 
 // Expert, row range and column offset of tile (mt, nt).
@@ -767,7 +742,7 @@ template <int BM, int ACT, int NSV>
 hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, const int32_t* offsets,
                  int E, const uint16_t* w, const uint16_t* b, uint16_t* c, uint16_t* cpre, int K,
                  int N, int Mt, int Nt, int SBN, int slots, float* part, hipEvent_t mid,
-                 hipStream_t s) {
+                 hipStream_t s, bool fixup) {
     const int units = std::min(slots, kMaxUnits);
     const dim3 block(256), grid((unsigned)((int64_t)Mt * Nt + units));
     if (cpre)
@@ -781,7 +756,7 @@ hipError_t launch_bf16(const uint16_t* x, uint32_t xb, const int32_t* rowmap, co
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && mid) e = hipEventRecord(mid, s);
     if (e != hipSuccess) return e;
-    if (part)
+    if (part && fixup)
         ffn_gemm_fixup<BM, ACT, NSV>
             <<<dim3((unsigned)(units / 2 * FixCfg<BM>::CHUNKS)), block, 0, s>>>(
                 offsets, E, b, c, cpre, K, N, Nt, SBN, slots, part);
@@ -811,7 +786,8 @@ bool gemm_dual(int bm, bool first) {
 template <int ACT>
 hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* rowmap,
                        const int32_t* offsets, const void* W, const void* bias, void* Cout,
-                       void* Cpre, int K, int N, float* part, hipEvent_t mid, hipStream_t s) {
+                       void* Cpre, int K, int N, float* part, hipEvent_t mid, hipStream_t s,
+                       bool fixup = true) {
     const int64_t rows = p.T * p.k;
     if (p.dtype == MOE_DTYPE_BF16) {
         const int bm = pick_bm(p);
@@ -832,19 +808,19 @@ hipError_t launch_gemm(const moe_problem_t& p, const void* X, const int32_t* row
         const bool dual = gemm_dual(bm, ACT != kActNone);
         if (bm == 256)
             e = launch_bf16<256, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
-                                         SBN, ncu, part, mid, s);
+                                         SBN, ncu, part, mid, s, fixup);
         else if (bm == 128 && dual)
             e = launch_bf16<128, ACT, 3>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
-                                         SBN, 2 * ncu, part, mid, s);
+                                         SBN, 2 * ncu, part, mid, s, fixup);
         else if (bm == 128)
             e = launch_bf16<128, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt,
-                                         SBN, ncu, part, mid, s);
+                                         SBN, ncu, part, mid, s, fixup);
         else if (dual)
             e = launch_bf16<64, ACT, 3>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN,
-                                        2 * ncu, part, mid, s);
+                                        2 * ncu, part, mid, s, fixup);
         else
             e = launch_bf16<64, ACT, 0>(x, xb, rowmap, offsets, p.E, w, b, c, cp, K, N, Mt, Nt, SBN,
-                                        ncu, part, mid, s);
+                                        ncu, part, mid, s, fixup);
         return e;
     } else {
         const int Mt = (int)((rows + 63) / 64 + p.E);
@@ -871,9 +847,23 @@ hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* 
 
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
-                           hipStream_t s) {
+                           hipStream_t s, bool fixup) {
     return launch_gemm<kActNone>(p, h, nullptr, offsets, W2, b2, y, nullptr, p.F, p.H, part, mid,
-                                 s);
+                                 s, fixup);
+}
+
+GemmCut down_gemm_cut(const moe_problem_t& p) {
+    // as launch_gemm picks them for the second GEMM (K = F, N = H)
+    GemmCut g;
+    g.bm = pick_bm(p);
+    const bool dual = g.bm <= 128 && gemm_dual(g.bm, false);
+    g.ns = dual ? 3 : g.bm == 256 ? Cfg<256>::NS : g.bm == 128 ? Cfg<128>::NS : Cfg<64>::NS;
+    const int bk = g.bm == 256 ? Cfg<256>::BK : g.bm == 128 ? Cfg<128>::BK : Cfg<64>::BK;
+    g.nk = (p.F + bk - 1) / bk;
+    g.Nt = gemm_nt(p.H);
+    g.SBN = (g.Nt % 16 == 0) ? 16 : (g.Nt % 8 == 0) ? 8 : 4;
+    g.ncu = dual ? 2 * device_cus() : device_cus();
+    return g;
 }
 
 size_t gemm_partial_bytes(const moe_problem_t& p) {

@@ -127,6 +127,59 @@ __device__ __forceinline__ void dense_coords(int p, int real_mt, int Nt, int SBN
     }
 }
 
+// Position p of tile (mt, nt) in the order above: the inverse of dense_coords
+// for 0 <= mt < real_mt, 0 <= nt < Nt, with SBN = 1 << lg (every division a
+// shift).
+__device__ __forceinline__ int dense_position(int mt, int nt, int real_mt, int Nt, int lg) {
+    const int SBN = 1 << lg, lm = 8 - lg;                 // SBM = 256 / SBN = 1 << lm
+    if (Nt & (SBN - 1)) return mt * Nt + nt;
+    const int F = real_mt >> lm;
+    if (mt < (F << lm)) {
+        const int sb = (mt >> lm) * (Nt >> lg) + (nt >> lg);
+        const int s8 = ((mt & ((1 << lm) - 1)) >> 3) + (((nt & (SBN - 1)) >> 2) << (lm - 3));
+        const int x = (s8 - sb) & 7;                                    // XCD of the sub-block
+        const int j = (mt & 7) + 8 * (nt & 3);                          // slot on the XCD
+        return (sb << 8) + x + 8 * j;
+    }
+    const int q0 = (F << lm) * Nt, rm = mt - (F << lm), rem = real_mt - (F << lm);
+    if ((Nt & 7) == 0) return q0 + (nt & 7) + 8 * ((nt >> 3) * rem + rm);
+    return q0 + rm * Nt + nt;
+}
+
+// How a grouped GEMM launch cuts its last round.  The R = real_mt * Nt real
+// tiles leave tail = R mod ncu tiles for a ragged last round; when those are
+// at most half of it, each is cut along K into S = ncu / tail slices (at most
+// kMaxUnits slices in all, each at least ns k-tiles deep), which write fp32
+// partial tiles; the positions [0, full) are computed whole.  The GEMM, its
+// fixup and the combine that finishes the second GEMM's cut tiles all take
+// the plan from here.
+constexpr int kMaxUnits = 256;
+
+struct TailPlan {
+    int real_mt;      // real row tiles
+    int full;         // tiles computed whole: positions [0, full)
+    int tail;         // tiles cut into S slices: positions [full, full + tail S)
+    int S;            // slices per tail tile (1: no cut)
+};
+
+__host__ __device__ __forceinline__ TailPlan plan_tail(int real_mt, int Nt, int ncu, int nk,
+                                                       int ns, bool allow) {
+    TailPlan pl;
+    pl.real_mt = real_mt;
+    const int R = real_mt * Nt;
+    pl.tail = R % ncu;
+    int S = pl.tail > 0 ? (ncu < kMaxUnits ? ncu : kMaxUnits) / pl.tail : 1;
+    if (nk / ns < S) S = nk / ns;
+    if (!allow || S < 2) {
+        pl.S = 1;
+        pl.tail = 0;
+    } else {
+        pl.S = S;
+    }
+    pl.full = R - pl.tail;
+    return pl;
+}
+
 // Real row tiles over all experts (every lane gets the same value).
 template <int BM>
 __device__ __forceinline__ int real_row_tiles(const int32_t* __restrict__ offsets, int E) {

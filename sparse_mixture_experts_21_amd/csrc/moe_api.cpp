@@ -271,10 +271,21 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     hipEvent_t up_fix = stage_events ? stage_events[MOE_EV_FFN_UP_FIXUP] : nullptr;
     hipEvent_t down_fix = stage_events ? stage_events[MOE_EV_FFN_DOWN_FIXUP] : nullptr;
     if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, hgrad, part, up_fix, stream);
+    // Inference (bf16): the combine finishes the second GEMM's cut tiles from
+    // their K-slice partials, so that GEMM needs no fixup launch.  Training
+    // keeps y whole for the backward.  Below 8 tokens the few workgroups of
+    // the combine would each wait on several serial rounds of slice loads (the
+    // GEMM is cut into up to 8 slices there), which the fixup's hundreds of
+    // workgroups do in one: those batches keep the fixup launch.
+    const bool cut_in_combine =
+        hgrad == nullptr && p->dtype == MOE_DTYPE_BF16 && p->T >= kCombineCutMinTokens;
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
-    if (e == hipSuccess) e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream);
+    if (e == hipSuccess)
+        e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream, !cut_in_combine);
     if (e == hipSuccess) e = ev(MOE_EV_COMBINE);
-    if (e == hipSuccess) e = launch_combine(*p, y, ps, tw, out, stream);
+    if (e == hipSuccess)
+        e = cut_in_combine ? launch_combine_cut(*p, y, ps, tw, idx, off, b2, part, out, stream)
+                           : launch_combine(*p, y, ps, tw, out, stream);
     if (e == hipSuccess) e = ev(MOE_EV_END);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

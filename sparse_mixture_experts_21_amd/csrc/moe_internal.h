@@ -96,14 +96,33 @@ hipError_t launch_route_small(const moe_problem_t& p, int64_t cap, const void* x
 hipError_t launch_ffn_up(const moe_problem_t& p, const void* xp, const int32_t* rowmap,
                          const int32_t* offsets, const void* W1, const void* b1, void* h,
                          void* hgrad, float* part, hipEvent_t mid, hipStream_t s);
+// fixup = false (bf16): the K-slice partials of the cut last round are left in
+// part for launch_combine_cut, and the cut tiles' rows of y are not written.
 hipError_t launch_ffn_down(const moe_problem_t& p, const void* h, const int32_t* offsets,
                            const void* W2, const void* b2, void* y, float* part, hipEvent_t mid,
-                           hipStream_t s);
+                           hipStream_t s, bool fixup = true);
 size_t gemm_partial_bytes(const moe_problem_t& p);
+// How the second (bf16) expert GEMM of p lays out its tiles and cuts its last
+// round: row tile height, LDS stages and k-tiles of the row layout, column
+// tiles, super-block width, workgroup slots.
+struct GemmCut {
+    int bm, ns, nk, Nt, SBN, ncu;
+};
+GemmCut down_gemm_cut(const moe_problem_t& p);
 // out[t] = sum over the k slots s of row t, in order, with pos[t][s] >= 0 of
 // topk_w[t][s] * y[pos[t][s]]; any k (expert choice passes k = E).
 hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* pos,
                           const float* topk_w, void* out, hipStream_t s);
+// The same for top-k routing (bf16) after launch_ffn_down(..., fixup = false):
+// a row of a cut tile is finished here from the K-slice partials in part (summed
+// in slice order, plus b2, rounded to bf16: the values the fixup would have
+// written to y), the other rows are read from y.  topk_idx gives each slot's
+// expert, offsets the experts' row ranges.
+constexpr int64_t kCombineCutMinTokens = 8;   // smallest batch that takes launch_combine_cut
+hipError_t launch_combine_cut(const moe_problem_t& p, const void* y, const int32_t* pos,
+                              const float* topk_w, const int32_t* topk_idx,
+                              const int32_t* offsets, const void* b2, const float* part,
+                              void* out, hipStream_t s);
 // ---- backward (bf16)
 hipError_t launch_gather(const moe_problem_t& p, const void* x, const int32_t* pos, void* xp,
                          hipStream_t s);
