@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -259,6 +260,63 @@ def cpu_baseline(spec, inp, limit_s: float):
     return {"value": spec.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu": cpu, "gflops": flops / (t_route + t_ffn) / 1e9, "seconds": t_route + t_ffn,
             "scaled": n != spec.T, "sample": sample}
+
+
+def _dense_coords(p, real_mt, Nt, SBN):
+    """Tile (mt, nt) at position p of the expert GEMMs' XCD-aware tile order
+    (the library's dense_coords, restated for the byte count below)."""
+    SBM = 256 // SBN
+    if Nt % SBN:
+        return p // Nt, p % Nt
+    F = real_mt // SBM
+    nfull = F * SBM * Nt
+    if p < nfull:
+        sb, q = p >> 8, p & 255
+        x, j = q & 7, q >> 3
+        nsbn = Nt // SBN
+        s8 = (x + sb) & 7
+        xm, xn = s8 % (SBM // 8), s8 // (SBM // 8)
+        return (sb // nsbn) * SBM + xm * 8 + (j & 7), (sb % nsbn) * SBN + xn * 4 + (j >> 3)
+    q, rem = p - nfull, real_mt - F * SBM
+    if Nt % 8 == 0:
+        x, j = q & 7, q >> 3
+        return F * SBM + j % rem, 8 * (j // rem) + x
+    return F * SBM + q // Nt, q % Nt
+
+
+def combine_cut_extra_bytes(T, k, E, H, F, cf, counts_kept, ncu):
+    """Bytes the combine of the top-k bf16 forward reads beyond a plain combine:
+    the second GEMM's cut tiles reach it as S fp32 K-slice partials instead of
+    bf16 y rows.  The plan follows the library: row tile height from the mean
+    expert load, the ragged last round of R = row tiles x column tiles cut into
+    S = min(min(ncu, 256) / tail, k-tiles / stages) slices when S >= 2."""
+    if T < 8:
+        return 0
+    cap = T if cf <= 0 else min(math.ceil(cf * T * k / E), T)
+    avg = min((T * k + E - 1) // E, cap)
+    bm = 64 if avg <= 32 else 128 if avg <= 128 else 256
+    bk, ns = (64, 2) if bm == 256 else (32, 4)
+    nk = (F + bk - 1) // bk
+    Nt = (H + 255) // 256
+    SBN = 16 if Nt % 16 == 0 else 8 if Nt % 8 == 0 else 4
+    tiles = [(int(n) + bm - 1) // bm for n in counts_kept]
+    real_mt = sum(tiles)
+    R = real_mt * Nt
+    tail = R % ncu
+    if tail == 0:
+        return 0
+    S = min(min(ncu, 256) // tail, nk // ns)
+    if S < 2:
+        return 0
+    first = [sum(tiles[:e]) for e in range(E)]          # row tiles before expert e
+    extra = 0
+    for p in range(R - tail, R):
+        mt, nt = _dense_coords(p, real_mt, Nt, SBN)
+        e = max(i for i in range(E) if first[i] <= mt and tiles[i] > 0)
+        rows = min(bm, int(counts_kept[e]) - (mt - first[e]) * bm)
+        cols = min(256, H - 256 * nt)
+        extra += rows * cols * (4 * S - 2)
+    return extra
 
 
 def routing_stats(E, counts, offsets, cap, T, k):
@@ -658,8 +716,13 @@ def main():
             # block histograms in, chunk bases out and back in, ids in, pos and
             # row_token out (the row gather is fused into ffn_up in moe_forward)
             "permute": 3 * nblk * E * 4 + T * k * 8 + A * 4,
-            # kept expert rows in, slot rows and weights in, token rows out
-            "combine": A * H * s + T * k * 8 + T * H * s,
+            # kept expert rows in, slot rows and weights in, token rows out; the
+            # second GEMM's cut tiles come in as fp32 K-slice partials
+            "combine": A * H * s + T * k * 8 + T * H * s + (
+                combine_cut_extra_bytes(T, k, E, H, F, spec.cf,
+                                        np.diff(offsets.cpu().numpy()),
+                                        torch.cuda.get_device_properties(0).multi_processor_count)
+                if spec.dtype == "bf16" else 0),
         }
     hbm = {n: {"ms": sm[n], "GB/s": alg_bytes[n] / (sm[n] * 1e-3) / 1e9,
                "frac": alg_bytes[n] / (sm[n] * 1e-3) / 1e9 / PEAK_HBM_GBS} for n in alg_bytes}

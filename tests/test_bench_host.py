@@ -1,6 +1,7 @@
 """Host logic of bench.py, on the CPU: kernel names as the counter summaries key
 them, the calibration of FETCH_SIZE / WRITE_SIZE by the copy kernel, the
-source-hash guard on stored traffic, the routing statistics, and the refusal
+source-hash guard on stored traffic, the routing statistics, the bytes the
+combine reads for the second GEMM's cut tiles, and the refusal
 of more than one GPU."""
 import csv
 import json
@@ -130,3 +131,57 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+# ---------------------------------------------------------------- combine bytes
+def _library_dense_coords(grids, tmp_path):
+    """dense_coords exactly as the library's gemm_common.h writes it, compiled
+    for the host, printing (mt, nt) for every position of each grid."""
+    src = open(os.path.join(ROOT, "sparse_mixture_experts_21_amd", "csrc", "gemm_common.h")).read()
+    i = src.index("__device__ __forceinline__ void dense_coords(")
+    j = src.index("{", i)
+    depth = 0
+    for end in range(j, len(src)):
+        depth += {"{": 1, "}": -1}.get(src[end], 0)
+        if depth == 0:
+            break
+    fn = src[i:end + 1].replace("__device__ __forceinline__", "static inline")
+    lines = "\n".join(f"    run({rm}, {nt}, {sbn});" for rm, nt, sbn in grids)
+    prog = ("#include <cstdio>\n" + fn + "\nstatic void run(int rm, int Nt, int SBN) {\n"
+            "    for (int p = 0; p < rm * Nt; ++p) { int mt, nt; dense_coords(p, rm, Nt, SBN, mt, nt);"
+            " printf(\"%d %d\\n\", mt, nt); }\n}\nint main() {\n" + lines + "\n    return 0;\n}\n")
+    c = tmp_path / "dc.cpp"
+    c.write_text(prog)
+    exe = tmp_path / "dc"
+    subprocess.run(["g++", "-O1", "-o", str(exe), str(c)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    return [(int(a), int(b)) for a, b in zip(out[0::2], out[1::2])]
+
+
+def test_dense_coords_restatement_matches_library(tmp_path):
+    grids = [(rm, nt, sbn) for sbn in (4, 8, 16) for nt in (1, 3, 4, 8, 16, 24, 56)
+             for rm in (1, 5, 17, 33, 64, 133)]
+    want = _library_dense_coords(grids, tmp_path)
+    got = [bench._dense_coords(p, rm, nt, sbn) for rm, nt, sbn in grids for p in range(rm * nt)]
+    assert got == want
+
+
+def test_combine_cut_extra_bytes_hand_case():
+    # Two experts of 300 rows: 256-row tiles (mean load 300), 2 row tiles each
+    # (256 and 44 rows), 3 column tiles (H = 768): 12 tiles, all in the ragged
+    # last round of 256 CUs, cut into min(256 // 12, 64 k-tiles // 2 stages) =
+    # 21 slices; each cut row reads 21 fp32 slices instead of one bf16 value.
+    extra = bench.combine_cut_extra_bytes(300, 2, 2, 768, 4096, 0.0, [300, 300], 256)
+    assert extra == 3 * 2 * (256 + 44) * 256 * (4 * 21 - 2)
+
+
+def test_combine_cut_extra_bytes_no_cut():
+    # below 8 tokens the forward keeps the fixup; a whole round has no tail;
+    # a tail above half a round is not cut
+    assert bench.combine_cut_extra_bytes(4, 2, 8, 4096, 14336, 0.0, [1] * 8, 256) == 0
+    assert bench.combine_cut_extra_bytes(8192, 2, 8, 1024, 4096, 0.0, [2048] * 8, 256) == 0
+    # 73 row tiles x 16 column tiles = 1168 = 4 rounds + 144 > 128
+    assert bench.combine_cut_extra_bytes(18688, 1, 1, 4096, 4096, 0.0, [18688], 256) == 0
+    # one more row tile on one expert: 65 x 16 = 1040 = 4 rounds + 16, cut into 16
+    assert bench.combine_cut_extra_bytes(8192, 2, 8, 4096, 4096, 0.0,
+                                         [2048] * 7 + [2049], 256) > 0
