@@ -290,8 +290,6 @@ def combine_cut_extra_bytes(T, k, E, H, F, cf, counts_kept, ncu):
     bf16 y rows.  The plan follows the library: row tile height from the mean
     expert load, the ragged last round of R = row tiles x column tiles cut into
     S = min(min(ncu, 256) / tail, k-tiles / stages) slices when S >= 2."""
-    if T < 8:
-        return 0
     cap = T if cf <= 0 else min(math.ceil(cf * T * k / E), T)
     avg = min((T * k + E - 1) // E, cap)
     bm = 64 if avg <= 32 else 128 if avg <= 128 else 256

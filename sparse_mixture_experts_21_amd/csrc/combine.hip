@@ -137,20 +137,26 @@ hipError_t launch_rows(const moe_problem_t& p, const void* y, const int32_t* pos
 // order in fp32.  The token's slot entries are loaded before the workgroup's
 // tile counts are reduced, so the two round trips overlap.  KM >= k slots are
 // held in registers (2 for top-1 and top-2, else kMaxK), which keeps the
-// kernel at several waves per SIMD.
-template <int BM, int KM, int TPT>
+// kernel at several waves per SIMD.  CV vectors per thread and pass; a token
+// row may span TPT / 256 workgroups (a few tokens: one vector per thread, so
+// that the slices of the whole row are loaded by many threads at once).
+// A cut vector's first slice and the next BATCH ones are loaded together.
+template <int BM, int KM, int TPT, int CV>
 __global__ __launch_bounds__(kCombThreads) void combine_rows_cut(
     const u32x4_t* __restrict__ y, const int32_t* __restrict__ pos,
     const float* __restrict__ topk_w, const int32_t* __restrict__ topk_idx, int k, int64_t T,
     int64_t vec, u32x4_t* __restrict__ out, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ bias, const float* __restrict__ part, GemmCut gc) {
     constexpr int UNIT = BM * 256;                        // floats of one partial tile
-    constexpr int BATCH = 4;                              // slice loads in flight
+    constexpr int BATCH = CV == 1 ? 8 : 4;                // slice loads in flight
+    constexpr int WPT = TPT > kCombThreads ? TPT / kCombThreads : 1;   // workgroups per token
     __shared__ int tb[kMaxE];                             // row tiles of the experts before e
     __shared__ int ofs[kMaxE];                            // the experts' first rows
     __shared__ int s_real_mt;
-    const int lane = threadIdx.x % TPT;
-    const int64_t t = (int64_t)blockIdx.x * (kCombThreads / TPT) + threadIdx.x / TPT;
+    const int lane = WPT > 1 ? (int)(blockIdx.x % WPT) * kCombThreads + (int)threadIdx.x
+                             : (int)threadIdx.x % TPT;
+    const int64_t t = WPT > 1 ? (int64_t)(blockIdx.x / WPT)
+                              : (int64_t)blockIdx.x * (kCombThreads / TPT) + threadIdx.x / TPT;
     const bool live = t < T;
     int32_t row[KM], ex[KM];
     float w[KM];
@@ -197,20 +203,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_cut(
         }
     }
     const int64_t H = vec * 8;
-    for (int64_t v0 = lane; v0 < vec; v0 += TPT * kCombVec) {
-        float acc[kCombVec][8];
+    for (int64_t v0 = lane; v0 < vec; v0 += TPT * CV) {
+        float acc[CV][8];
 #pragma unroll
-        for (int u = 0; u < kCombVec; ++u)
+        for (int u = 0; u < CV; ++u)
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc[u][q] = 0.f;
         // float offset of the vector's first slice in part, or -1: read y
-        int32_t cut[KM][kCombVec];
-        u32x4_t d[KM][kCombVec];
+        int32_t cut[KM][CV];
+        u32x4_t d[KM][CV];
 #pragma unroll
         for (int s = 0; s < KM; ++s) {
             if (row[s] < 0) continue;                     // uniform: no divergence
 #pragma unroll
-            for (int u = 0; u < kCombVec; ++u) {
+            for (int u = 0; u < CV; ++u) {
                 const int64_t v = v0 + (int64_t)u * TPT;
                 cut[s][u] = -1;
                 if (v >= vec) continue;
@@ -226,12 +232,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_cut(
         for (int s = 0; s < KM; ++s) {
             if (row[s] < 0) continue;
 #pragma unroll
-            for (int u = 0; u < kCombVec; ++u) {
+            for (int u = 0; u < CV; ++u) {
                 if (cut[s][u] < 0) continue;
                 const float* src = part + cut[s][u];
                 f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src);
                 f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + 4);
                 for (int sb = 1; sb < pl.S; sb += BATCH) {
+                    // (independent of slice 0's loads, so both are in flight together)
                     // unconditional loads at clamped slice indices, masked in the sum
                     f32x4_t t0[BATCH], t1[BATCH];
 #pragma unroll
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_cut(
             }
         }
 #pragma unroll
-        for (int u = 0; u < kCombVec; ++u) {
+        for (int u = 0; u < CV; ++u) {
             const int64_t v = v0 + (int64_t)u * TPT;
             if (v >= vec) continue;
 #pragma unroll
@@ -302,17 +309,27 @@ hipError_t launch_combine_cut(const moe_problem_t& p, const void* y, const int32
     auto* yv = static_cast<const u32x4_t*>(y);
     auto* ov = static_cast<u32x4_t*>(out);
     auto* bb = static_cast<const uint16_t*>(b2);
-    auto go = [&](auto bm, auto km, auto tpt) {
+    auto go = [&](auto bm, auto km, auto tpt, auto cv) {
         constexpr int BM = decltype(bm)::value, KM = decltype(km)::value;
-        constexpr int TPT = decltype(tpt)::value;
-        const unsigned nb = (unsigned)((p.T + (kCombThreads / TPT) - 1) / (kCombThreads / TPT));
-        combine_rows_cut<BM, KM, TPT><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
+        constexpr int TPT = decltype(tpt)::value, CV = decltype(cv)::value;
+        const unsigned nb = TPT > kCombThreads
+            ? (unsigned)(p.T * (TPT / kCombThreads))
+            : (unsigned)((p.T + (kCombThreads / TPT) - 1) / (kCombThreads / TPT));
+        combine_rows_cut<BM, KM, TPT, CV><<<dim3(nb), dim3(kCombThreads), 0, s>>>(
             yv, pos, topk_w, topk_idx, p.k, p.T, vec, ov, offsets, p.E, bb, part, gc);
     };
+    using I = std::integral_constant<int, 1>;
+    using II = std::integral_constant<int, kCombVec>;
     auto pick_tpt = [&](auto bm, auto km) {
-        if (vec > 128 * kCombVec) go(bm, km, std::integral_constant<int, 256>{});
-        else if (vec > 64 * kCombVec) go(bm, km, std::integral_constant<int, 128>{});
-        else go(bm, km, std::integral_constant<int, 64>{});
+        if (p.T < kCombineCutWideBelow) {
+            // a few tokens: one vector per thread, the row over up to 4 workgroups
+            if (vec > 512) go(bm, km, std::integral_constant<int, 1024>{}, I{});
+            else if (vec > 256) go(bm, km, std::integral_constant<int, 512>{}, I{});
+            else if (vec > 128) go(bm, km, std::integral_constant<int, 256>{}, I{});
+            else go(bm, km, std::integral_constant<int, 128>{}, I{});
+        } else if (vec > 128 * kCombVec) go(bm, km, std::integral_constant<int, 256>{}, II{});
+        else if (vec > 64 * kCombVec) go(bm, km, std::integral_constant<int, 128>{}, II{});
+        else go(bm, km, std::integral_constant<int, 64>{}, II{});
     };
     auto pick_km = [&](auto bm) {
         if (p.k <= 2) pick_tpt(bm, std::integral_constant<int, 2>{});

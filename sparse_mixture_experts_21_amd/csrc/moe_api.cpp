@@ -273,10 +273,7 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     if (e == hipSuccess) e = launch_ffn_up(*p, x, rt, off, W1, b1, h, hgrad, part, up_fix, stream);
     // Inference (bf16): the combine finishes the second GEMM's cut tiles from
     // their K-slice partials, so that GEMM needs no fixup launch.  Training
-    // keeps y whole for the backward.  Below 8 tokens the few workgroups of
-    // the combine would each wait on several serial rounds of slice loads (the
-    // GEMM is cut into up to 8 slices there), which the fixup's hundreds of
-    // workgroups do in one: those batches keep the fixup launch.
+    // keeps y whole for the backward.
     const bool cut_in_combine =
         hgrad == nullptr && p->dtype == MOE_DTYPE_BF16 && p->T >= kCombineCutMinTokens;
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);

@@ -166,6 +166,13 @@ def test_dense_coords_restatement_matches_library(tmp_path):
     assert got == want
 
 
+def test_combine_cut_extra_bytes_decode():
+    # one token to experts 0 and 1: 2 one-row tiles x 16 column tiles, all cut
+    # into min(256 // 32, 448 k-tiles // 4 stages) = 8 slices
+    extra = bench.combine_cut_extra_bytes(1, 2, 8, 4096, 14336, 0.0, [1, 1, 0, 0, 0, 0, 0, 0], 256)
+    assert extra == 2 * 16 * 1 * 256 * (4 * 8 - 2)
+
+
 def test_combine_cut_extra_bytes_hand_case():
     # Two experts of 300 rows: 256-row tiles (mean load 300), 2 row tiles each
     # (256 and 44 rows), 3 column tiles (H = 768): 12 tiles, all in the ragged
@@ -176,9 +183,7 @@ def test_combine_cut_extra_bytes_hand_case():
 
 
 def test_combine_cut_extra_bytes_no_cut():
-    # below 8 tokens the forward keeps the fixup; a whole round has no tail;
-    # a tail above half a round is not cut
-    assert bench.combine_cut_extra_bytes(4, 2, 8, 4096, 14336, 0.0, [1] * 8, 256) == 0
+    # a whole round has no tail; a tail above half a round is not cut
     assert bench.combine_cut_extra_bytes(8192, 2, 8, 1024, 4096, 0.0, [2048] * 8, 256) == 0
     # 73 row tiles x 16 column tiles = 1168 = 4 rounds + 144 > 128
     assert bench.combine_cut_extra_bytes(18688, 1, 1, 4096, 4096, 0.0, [18688], 256) == 0

@@ -160,7 +160,7 @@ CUT = [
 ]
 
 
-@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[1:3] + FEW[1:3] + RES[:1] + WIDE[1:2]
+@pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[:3] + FEW[:3] + RES[:1] + WIDE[1:2]
                          + [SMALL[9]] + CUT, ids=lambda s: s.name)
 def test_stages_equal_forward_bitwise(spec):
     say(f"[stages == forward] {spec.name}")
