@@ -31,7 +31,9 @@
 // Load balance: when the real tiles leave a ragged last round of at most half
 // the workgroup slots, those tiles are cut along K into slices that fill one whole round
 // and write fp32 partials; ffn_gemm_fixup sums them in slice order and applies
-// the epilogue (bias, activation, bf16).
+// the epilogue (bias, activation, bf16).  In the inference forward the second
+// GEMM's partials go to the combine instead, which does the same for the
+// rows it reads (launch_ffn_down with fixup = false).
 #include <type_traits>
 
 #include "moe_internal.h"

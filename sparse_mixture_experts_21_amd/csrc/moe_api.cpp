@@ -274,8 +274,7 @@ moe_status_t forward_impl(const moe_problem_t& P, const WsLayout& L, char* w, co
     // Inference (bf16): the combine finishes the second GEMM's cut tiles from
     // their K-slice partials, so that GEMM needs no fixup launch.  Training
     // keeps y whole for the backward.
-    const bool cut_in_combine =
-        hgrad == nullptr && p->dtype == MOE_DTYPE_BF16 && p->T >= kCombineCutMinTokens;
+    const bool cut_in_combine = hgrad == nullptr && p->dtype == MOE_DTYPE_BF16;
     if (e == hipSuccess) e = ev(MOE_EV_FFN_DOWN);
     if (e == hipSuccess)
         e = launch_ffn_down(*p, h, off, W2, b2, y, part, down_fix, stream, !cut_in_combine);

@@ -118,7 +118,6 @@ hipError_t launch_combine(const moe_problem_t& p, const void* y, const int32_t* 
 // in slice order, plus b2, rounded to bf16: the values the fixup would have
 // written to y), the other rows are read from y.  topk_idx gives each slot's
 // expert, offsets the experts' row ranges.
-constexpr int64_t kCombineCutMinTokens = 1;   // smallest batch that takes launch_combine_cut
 constexpr int64_t kCombineCutWideBelow = 8;   // below this, one vector per thread (wide rows)
 hipError_t launch_combine_cut(const moe_problem_t& p, const void* y, const int32_t* pos,
                               const float* topk_w, const int32_t* topk_idx,
