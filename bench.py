@@ -63,6 +63,11 @@ def parse():
                          "(torch.bmm, hipBLASLt) on the workload's two expert GEMM shapes with "
                          "balanced experts, each for about SECONDS, one JSON line (a side "
                          "reference for the expert GEMMs; the library is not called)")
+    ap.add_argument("--vendor-stream", type=float, default=0.0, metavar="SECONDS",
+                    help="instead of the layer: time the runtime's device-to-device copy and "
+                         "torch's sum over a buffer the size of the workload's x, each for "
+                         "about SECONDS, one JSON line (the practical HBM rate the router's "
+                         "read of x is held against; the library is not called)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "WRITE_SIZE, both with --calibrate-copy) into "
@@ -192,6 +197,37 @@ def vendor_gemm(spec, seconds: float):
         res[name] = {"calls": n, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
                      "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del a, b, c
+    return res
+
+
+def vendor_stream(spec, seconds: float):
+    """Plain streams over a buffer of the workload's x size (T x H bf16): the
+    runtime's device-to-device copy (reads and writes every byte) and torch's
+    sum (reads every byte once), each timed with HIP events over back-to-back
+    calls."""
+    import torch
+    n = spec.T * spec.H
+    x = torch.randn(n, device="cuda", dtype=torch.bfloat16)
+    dst = torch.empty_like(x)
+    acc = torch.empty((), device="cuda", dtype=torch.float32)
+    res = {"workload": spec.name, "bytes": 2 * n}
+    for name, fn, moved in (("copy", lambda: dst.copy_(x), 4 * n),
+                            ("sum", lambda: torch.sum(x, dim=0, dtype=torch.float32, out=acc), 2 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        calls, t0 = 0, time.perf_counter()
+        e0.record()
+        while calls < 20 or time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            calls += 20
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        res[name] = {"calls": calls, "us": us, "GB/s": moved / (us * 1e-6) / 1e9,
+                     "frac_of_8TBs": moved / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     return res
 
 
@@ -565,6 +601,9 @@ def main():
     spec = W.CONFIGS[args.config]
     if args.vendor_gemm > 0:
         print(json.dumps(vendor_gemm(spec, args.vendor_gemm)), flush=True)
+        return
+    if args.vendor_stream > 0:
+        print(json.dumps(vendor_stream(spec, args.vendor_stream)), flush=True)
         return
     moe.lib()
 
