@@ -157,7 +157,21 @@ CUT = [
     S("cut_T8192_H1024_E8_k2_F1024_cf1.25", 8192, 1024, 8, 2, 1024, cf=1.25, biases=True),
     S("cut_T4096_H2048_E8_k2_F512", 4096, 2048, 8, 2, 512, biases=True,
       bg=W.Dist("zipf_log", 1.2)),
+    # 16-wide super-blocks (80 of 336 tiles cut into 3); a column count no
+    # super-block width divides (5: the plain order, 120 tiles in 2); the
+    # 128-row layout (128 of 384 in 2) and the 64-row layout (128 of 384 in 2)
+    S("cut_T2048_H4096_E8_k2_F512", 2048, 4096, 8, 2, 512, biases=True),
+    S("cut_T2500_H1280_E8_k2_F512", 2500, 1280, 8, 2, 512, biases=True),
+    S("cut_T1500_H3072_E32_k2_F256", 1500, 3072, 32, 2, 256, wg=W.Dist("normal", 0.1)),
+    S("cut_T800_H1536_E64_k2_F512", 800, 1536, 64, 2, 512, biases=True,
+      wg=W.Dist("normal", 0.1)),
 ]
+
+
+@pytest.mark.parametrize("spec", CUT, ids=lambda s: s.name)
+def test_forward_cut_all_outputs(spec):
+    """The shapes above end to end against the oracle at every token."""
+    test_forward_small_all_outputs(spec)
 
 
 @pytest.mark.parametrize("spec", SMALL[:8] + SILU[:2] + TINY[:3] + FEW[:3] + RES[:1] + WIDE[1:2]
