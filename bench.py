@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--train", action="store_true",
                     help="time a training step instead: moe_forward_train then moe_backward "
                          "(aux and z loss weights 0.01 and 0.001), one JSON line")
+    ap.add_argument("--no-vendor-reference", action="store_true",
+                    help="skip the same-machine side references appended to the JSON line "
+                         "(the vendor batched GEMM on the expert shapes, plain streams over x)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the forward replayed as a captured HIP graph")
     ap.add_argument("--no-abi-timing", action="store_true",
@@ -824,6 +827,13 @@ def main():
         res["cpu_baseline"] = cpu_baseline(spec, inp, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    # Context from the same machine, after the timed work: the vendor library's
+    # batched GEMM on the expert shapes (balanced experts) and plain streams
+    # over a buffer of x's size.  Not part of the layer or of its figures.
+    if not args.no_vendor_reference and spec.dtype == "bf16" and T * k // E >= 256:
+        log("[bench] vendor side references (torch.bmm, copy, sum)")
+        res["vendor_reference"] = {"gemm": vendor_gemm(spec, 1.0),
+                                   "stream": vendor_stream(spec, 0.5)}
     print(json.dumps(res), flush=True)
 
 
